@@ -1,0 +1,209 @@
+"""Benchmark of the per-head KV retention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+One step = the whole prefill path over one batch of synthetic input already
+resident in HBM: hubkv_score -> hubkv_refine -> hubkv_select -> hubkv_compact
+(every KV head, every layer of the workload).  Prints one JSON line with
+scored+selected tokens per second per head, per-op times measured with HIP
+events on the launch stream, the roofline position of the dominant op, and
+the CPU oracle timed on this host's cores on a bounded sample.
+
+Default workload: the Llama-2-7B-shaped layer (32 MHA heads, d 128, 32768
+tokens, window 64, 10% kept with 4 sink and 64 recent tokens, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+
+
+def _cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def op_bytes(w, kept_total, elem):
+    """Algorithmic HBM bytes of each op for one step (every layer and head)."""
+    L, Hkv, Hq, d, T, W, B = w.L, w.Hkv, w.Hq, w.d, w.T, w.W, w.B
+    q = L * Hq * B * W * d * elem
+    k = L * Hkv * T * d * elem
+    s = L * Hkv * T * 4
+    idx = L * Hkv * kept_total * 4
+    rows = L * Hkv * kept_total * d * elem
+    return {
+        "score": q + k + s,                 # Q and K read once, s written
+        "refine": 2 * s,                    # s read, z written
+        "select": s + idx,                  # z read, indices written
+        "compact": idx + 4 * rows,          # indices read, K and V rows read and written
+    }
+
+
+def score_flops(w):
+    """One QK^T sweep (2 flops per multiply-add; the causal corner is ignored)."""
+    return 2.0 * w.L * w.Hq * w.W * w.T * w.d
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU mode: every (layer, sequence, KV head) unit is independent, so N GPUs "
+              "would each run this same kernel chain on their own share of heads.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    import token_scoring_top_amd as hk
+
+    hk.lib()  # fails loudly when the native library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = S.workload(args.workload)
+    if not isinstance(w, S.PrefillWorkload):
+        raise SystemExit("bench.py times the prefill path; pick a prefill workload")
+    nthreads = min(16, _cores())
+    Q, K, V = S.prefill_inputs(w, threads=nthreads)
+    elem = 2 if w.dtype == "bf16" else 4
+
+    def dev(x):
+        if w.dtype == "bf16":
+            bits = S.to_bf16_bits(x).view(np.int16)
+            return torch.from_numpy(np.ascontiguousarray(bits)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    kept = w.kept()
+    Ksum = int(kept.sum())
+    L, Hkv, T = w.L, w.Hkv, w.T
+    f32 = dict(dtype=torch.float32, device="cuda")
+    s = torch.empty((L, Hkv, T), **f32)
+    z = torch.empty((L, Hkv, T), **f32)
+    st = torch.empty((L, w.B, Hkv, 2), dtype=torch.float64, device="cuda")
+    beta = torch.empty((L, w.B, Hkv), **f32)
+    idx = torch.empty((L, Hkv, Ksum), dtype=torch.int32, device="cuda")
+    ko = torch.empty((L, Hkv, Ksum, w.d), dtype=Kd.dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    sl = hk._arr64(w.seqlens)
+    ws_s = torch.empty(hk.lib().hubkv_score_workspace(w.B, sl, L, w.Hq, Hkv, w.W, w.d,
+                                                      1 if elem == 2 else 0),
+                       dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(max(256, hk.lib().hubkv_refine_workspace(w.B, sl, L, Hkv)),
+                       dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal, s=s, head_stats=st,
+                       workspace=ws_s, stream=stream)
+        if ev: ev[1].record(stream)
+        hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                        beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
+                        workspace=ws_r, stream=stream)
+        if ev: ev[2].record(stream)
+        hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent, idx=idx, stream=stream)
+        if ev: ev[3].record(stream)
+        hk.hubkv_compact(Kd, Vd, idx, w.seqlens, kept, k_out=ko, v_out=vo, stream=stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["score", "refine", "select", "compact"]
+    op_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+             for j, n in enumerate(names)}
+    tokens = float(w.T * w.L)
+    value = tokens / (ms_step / 1e3)
+
+    nb = op_bytes(w, Ksum, elem)
+    dom = max(op_ms, key=op_ms.get)
+    ach = nb[dom] / (op_ms[dom] / 1e3) / 1e9
+    rsc_bytes = nb["refine"] + nb["select"] + nb["compact"]
+    rsc_ms = op_ms["refine"] + op_ms["select"] + op_ms["compact"]
+    mfma_util = score_flops(w) / (op_ms["score"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12)
+    kernels = {"score": "score_stats_mfma + score_combine + score_probs_mfma + stats_final",
+               "refine": "beta_kernel + refine_kernel", "select": "select_kernel",
+               "compact": "compact_kernel"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.set_threads(nthreads)
+        used = oracle.get_threads()
+        # bounded sample: whole prefill chains of this workload, repeated for
+        # about the CPU budget (at least one)
+        reps, tc0 = 0, time.perf_counter()
+        while True:
+            oracle.prefill_chain(Q, K, V, w)
+            reps += 1
+            if time.perf_counter() - tc0 >= args.cpu_budget_s or reps >= 50:
+                break
+        tc = (time.perf_counter() - tc0) / reps
+        cpu = {"value": tokens / tc, "unit": "tokens/s/head", "cores": used, "kind": "oracle",
+               "sample": f"{reps} full prefill chain(s) of this workload "
+                         f"({w.Hkv} heads x {w.T} tokens), {tc:.2f} s each"}
+
+    out = {
+        "metric": "scored+selected KV tokens/sec per head",
+        "value": value,
+        "unit": "tokens/s/head",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "seqlens": list(w.seqlens), "layers": w.L, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "d": w.d, "window": w.W, "budget": w.budget, "r": w.r,
+                   "n_sink": w.n_sink, "n_recent": w.n_recent, "kept_per_head": int(Ksum),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": dom,
+                     "kernels": kernels[dom], "algorithmic_bytes": nb[dom]},
+        "ops_ms": op_ms,
+        "refine_select_compact": {"ms": rsc_ms, "bytes": rsc_bytes,
+                                  "GBs": rsc_bytes / (rsc_ms / 1e3) / 1e9,
+                                  "frac_hbm": rsc_bytes / (rsc_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "score_mfma": {"flops_one_sweep": score_flops(w), "util": mfma_util,
+                       "peak_tflops": BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,203 @@
+/*
+ * hubkv.h -- C ABI of the MI355X (gfx950) KV-cache retention library.
+ *
+ * The library computes, per KV head, which cached tokens a long-context
+ * decoder keeps:
+ *   hubkv_score    base scores: attention mass of an observation window
+ *   hubkv_refine   HubKV refinement of those scores before Top-K
+ *   hubkv_select   per-head Top-K with protected sink and recent tokens
+ *   hubkv_compact  gather of the kept K/V rows into a packed cache
+ *   h2o_step       one streaming (decode) step of H2O greedy eviction
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE memory unless the parameter says "host".
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream) and never synchronises it.
+ *   - The library never allocates device memory and keeps no mutable global
+ *     state.  Scratch space is a caller-provided workspace whose size comes
+ *     from the matching *_workspace() query; it must stay alive until the
+ *     enqueued work has finished.
+ *   - Host arrays (sequence lengths, kept counts, positions) are read during
+ *     the call only.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     validation error nothing is launched, outputs are untouched and a
+ *     negative status is returned.  A failed launch returns HUBKV_EHIP and the
+ *     HIP error code is kept per thread (hubkv_last_hip_error).  Faults inside
+ *     kernels surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ *
+ * Layouts (row-major, the head dimension d contiguous; T = sum of sequence
+ * lengths; sequences are packed one after another along the token axis):
+ *   Q        [L][Hq][B*W][d]     queries of the last W positions of each sequence
+ *   K, V     [L][Hkv][T][d]
+ *   s, z     [L][Hkv][T]         fp32
+ *   stats    [L][B][Hkv][2]      fp64 {sum_i s_i, sum_i s_i ln s_i}
+ *   beta     [L][B][Hkv]         fp32
+ *   idx      [L][Hkv][sum_b kept_b]  int32, positions local to their sequence,
+ *                                ascending within each sequence
+ *   K_out, V_out [L][Hkv][sum_b kept_b][d]
+ * Query head h belongs to KV head h / (Hq / Hkv) (contiguous groups).
+ *
+ * Limits: 1 <= B <= 64; d in {64, 128}; Hq % Hkv == 0; (Hq/Hkv)*W <= 512;
+ * W <= every sequence length; element type HUBKV_F32 or HUBKV_BF16; Q/K/V
+ * base pointers 16-byte aligned, fp32/int32 arrays 4-byte aligned, fp64
+ * arrays 8-byte aligned.
+ *
+ * Page references are to the public pages this method is described on: the
+ * "HubKV walkthrough" page, the "H2O breakdown" page (a walk-through of the
+ * heavy-hitter oracle paper) and a general KV-cache survey page.
+ */
+#ifndef HUBKV_H
+#define HUBKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define HUBKV_OK 0
+#define HUBKV_EINVAL (-1)     /* a size, count or parameter is out of range      */
+#define HUBKV_EDTYPE (-2)     /* unsupported element type or head dimension      */
+#define HUBKV_EALIGN (-3)     /* a pointer is null or not aligned as required    */
+#define HUBKV_EWORKSPACE (-4) /* workspace missing or smaller than required      */
+#define HUBKV_EHIP (-5)       /* a HIP launch failed; see hubkv_last_hip_error() */
+
+/* Element types of Q, K and V. */
+#define HUBKV_F32 0
+#define HUBKV_BF16 1
+
+/* Workspace bytes hubkv_score needs for this problem (0 on invalid sizes). */
+size_t hubkv_score_workspace(int B, const int64_t* seqlens /* host [B] */, int L, int Hq, int Hkv,
+                             int W, int d, int dtype);
+
+/*
+ * hubkv_score -- base retention score of every cached token.
+ *
+ * H2O breakdown page, "Observation 2": a token's importance is the attention
+ * probability it accumulates over query positions.  KV-cache survey page,
+ * section 1.1: the attention is softmax(q K^T / sqrt(d_head)); section 4.3:
+ * SnapKV reads this pattern from the prefill queries.  Here the queries are
+ * the last W positions of each sequence:
+ *   s[l][g][i] = sum over the query heads h of group g and window rows w of
+ *                softmax_i( scale * q[l][h][w] . k[l][g][i] ),
+ * the softmax over keys i <= N_b - W + w when causal != 0, else over all N_b.
+ * head_stats (nullable) receives {sum_i s_i, sum_i s_i ln s_i} per
+ * (layer, sequence, KV head); hubkv_refine derives the head weight from it.
+ *
+ * q, k: element type dtype.  s: fp32 [L][Hkv][T].  workspace: at least
+ * hubkv_score_workspace() bytes, 256-byte aligned.
+ */
+int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens /* host */,
+                int L, int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                double* head_stats /* nullable */, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace bytes hubkv_refine needs (0 on invalid sizes). */
+size_t hubkv_refine_workspace(int B, const int64_t* seqlens /* host [B] */, int L, int Hkv);
+
+/*
+ * hubkv_refine -- HubKV score refinement before Top-K (HubKV walkthrough,
+ * "Method": four steps applied to the base scores, per head):
+ *   1 local hubs: token i is a hub when s_i equals the maximum of s over the
+ *     window [i - pool/2, i + pool/2] of its own sequence (max-pooling, width
+ *     5 on the page; the window is cut at the sequence ends; equal maxima are
+ *     all hubs);
+ *   2 SMD discount: q_i = s_i for hubs, gamma * s_i otherwise (gamma = 0.5);
+ *   3 head calibration: beta_h = clip(sel_h / mean over the layer's KV heads
+ *     of sel, beta_lo, beta_hi) with selectivity sel_h = 1 - H(s_h / sum s_h)
+ *     / ln N_b (the page asks for a mild, selectivity-based weight clipped to
+ *     [0.8, 1.2]); beta_h = 1 when the mean selectivity is not positive;
+ *   4 ratio gate: z_i = s_i + r^2 (beta_h q_i - s_i), computed in fp32 as
+ *     fma(fl(r*r), fl(beta*q) - s, s).
+ * beta comes from beta_in when it is non-null, else from head_stats when it
+ * is non-null, else from statistics computed here from s.
+ * s, z: fp32 [L][Hkv][T], z must not alias s.  beta_out (nullable) receives
+ * the beta used.  pool odd, 1 <= pool <= 63; 0 < gamma <= 1; beta_lo <= beta_hi;
+ * 0 <= r <= 1; Hkv <= 1024.
+ */
+int hubkv_refine(const float* s, int B, const int64_t* seqlens /* host */, int L, int Hkv,
+                 const double* head_stats /* nullable */, const float* beta_in /* nullable */,
+                 int pool, float gamma, float beta_lo, float beta_hi, float r, float* z,
+                 float* beta_out /* nullable */, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * hubkv_select -- per-head Top-K with protected windows.
+ *
+ * HubKV walkthrough: refined scores go to ordinary Top-K pruning, which
+ * maximises the modular sum of kept scores.  H2O breakdown page, heavy +
+ * recent and per-head sections; KV-cache survey page, sections 4.1-4.2: the
+ * first n_sink tokens and the last n_recent tokens of every sequence are
+ * always kept.  For each (layer, KV head, sequence b) the kept set is those
+ * protected positions plus the kept[b] - |protected| unprotected positions
+ * with the largest z, ties to the lower position, NaN lowest, -0 == +0.  The
+ * set is written ascending to idx at offset sum_{b' < b} kept[b'].
+ * kept: host [B], |protected_b| <= kept[b] <= N_b.  The result is
+ * deterministic.
+ */
+int hubkv_select(const float* z, int B, const int64_t* seqlens /* host */, int L, int Hkv,
+                 const int64_t* kept /* host [B] */, int n_sink, int n_recent, int32_t* idx,
+                 void* stream);
+
+/*
+ * hubkv_compact -- physically drop evicted tokens (H2O breakdown page, "two
+ * code bases": the real-drop variant removes the evicted K/V rows):
+ *   K_out[l][g][o_b + j] = K[l][g][cu_b + idx[l][g][o_b + j]], same for V,
+ * with cu_b the first token of sequence b and o_b = sum_{b' < b} kept[b'].
+ * A bit copy of whole rows; idx as produced by hubkv_select (values must lie
+ * in [0, N_b); out-of-range entries are skipped, their rows left untouched).
+ */
+int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
+                  const int64_t* seqlens /* host */, const int64_t* kept /* host [B] */, int L,
+                  int Hkv, int d, void* k_out, void* v_out, void* stream);
+
+/*
+ * h2o_step -- one decode step of H2O greedy eviction on a fixed-slot cache.
+ *
+ * H2O breakdown page, "greedy eviction" (Algorithm 1 description), the heavy
+ * + recent section and the FlexGen section (preallocated slots; the evicted
+ * token's slot is overwritten by the new token; accumulated scores ride on
+ * the attention computation).  Independently per (sequence b, KV head g):
+ *   p_h   = softmax over the occupied slots (and the new token itself when
+ *           include_self != 0) of scale * q[b][h] . k_cache[b][g][slot], for
+ *           the query heads h of the group;
+ *   acc  += sum_h p_h on the occupied slots;
+ *   the new token t[b] enters with acc = include_self ? sum_h p_h(new) : 0;
+ *   if a slot is empty (pos < 0) the lowest such slot takes it; otherwise the
+ *   token with the smallest acc among positions in [n_sink, t - n_recent]
+ *   (the new token included when it qualifies) is evicted, ties to the
+ *   oldest position, and its slot takes the new token (K/V row, acc, pos).
+ * q [B][Hq][d], k_new/v_new [B][Hkv][d] (dtype); k_cache/v_cache
+ * [B][Hkv][C][d] (dtype), acc fp32 and pos int32 [B][Hkv][C] (-1 = empty),
+ * all updated in place.  t: host [B] positions of the new tokens.
+ * evicted (nullable) [B][Hkv]: evicted position or -1.  probs (nullable)
+ * [B][Hq][C+1] fp32: this step's probabilities per slot (0 for empty slots)
+ * and, last, the new token's own probability.
+ * Requires C >= n_sink + n_recent, Hq/Hkv <= 16 and (Hq/Hkv) * C <= 12288.
+ */
+int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+             void* v_cache, float* acc, int32_t* pos, const int64_t* t /* host [B] */, int B,
+             int Hq, int Hkv, int d, int C, int n_sink, int n_recent, float scale,
+             int include_self, int32_t* evicted /* nullable */, float* probs /* nullable */,
+             void* stream);
+
+/* Number of protected positions of a sequence of length N (host helper). */
+int64_t hubkv_protected_count(int64_t N, int n_sink, int n_recent);
+
+/* Static text for a status code. */
+const char* hubkv_strerror(int status);
+
+/* hipError_t behind the calling thread's last HUBKV_EHIP (0 if none). */
+int hubkv_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int hubkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HUBKV_H */

@@ -1,0 +1,166 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/hubkv.h declares, and
+reject invalid arguments on the host before anything reaches the GPU.  The
+calls below that pass non-null fake pointers always carry some invalid
+argument, so validation returns before any HIP call is made.
+"""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+import oracle
+import token_scoring_top_amd as hk
+
+EINVAL, EDTYPE, EALIGN, EWS = -1, -2, -3, -4
+P = 0x10000  # fake, 256-aligned "device" pointer; never dereferenced
+
+
+def a64(xs):
+    return (C.c_int64 * len(xs))(*xs)
+
+
+def test_library_exports_every_declared_function():
+    L = hk.lib()
+    names = hk.header_functions()
+    assert {"hubkv_score", "hubkv_refine", "hubkv_select", "hubkv_compact", "h2o_step"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.hubkv_version() >= 100
+
+
+def test_strerror_and_last_error():
+    L = hk.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.hubkv_strerror(code)
+    assert L.hubkv_last_hip_error() == 0
+
+
+def test_protected_count_matches_oracle():
+    for N in (1, 5, 20, 100, 4096):
+        for ns in (0, 1, 4, 50):
+            for nr in (0, 3, 64, 200):
+                assert hk.protected_count(N, ns, nr) == oracle.protected_count(N, ns, nr)
+
+
+def test_workspace_queries():
+    L = hk.lib()
+    sl = a64([32768])
+    assert L.hubkv_score_workspace(1, sl, 1, 32, 32, 64, 128, 1) > 0
+    assert L.hubkv_score_workspace(1, sl, 1, 32, 32, 64, 96, 1) == 0      # bad d
+    assert L.hubkv_score_workspace(1, sl, 1, 32, 8, 256, 128, 1) == 0     # G*W > 512
+    assert L.hubkv_score_workspace(1, a64([10]), 1, 4, 4, 32, 64, 0) == 0  # W > N
+    assert L.hubkv_refine_workspace(1, sl, 1, 32) > 0
+    assert L.hubkv_refine_workspace(0, sl, 1, 32) == 0
+
+
+def test_score_validation():
+    L = hk.lib()
+    sl = a64([512])
+    big = 1 << 30
+    ok = dict(q=P, k=P, dt=0, B=1, sl=sl, L=1, Hq=4, Hkv=4, W=32, d=64, scale=0.125, causal=1,
+              s=P, st=P, ws=P, wsb=big, stream=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.hubkv_score(a["q"], a["k"], a["dt"], a["B"], a["sl"], a["L"], a["Hq"], a["Hkv"],
+                             a["W"], a["d"], a["scale"], a["causal"], a["s"], a["st"], a["ws"],
+                             a["wsb"], a["stream"])
+
+    assert call(dt=7) == EDTYPE
+    assert call(d=96) == EDTYPE
+    assert call(Hq=6) == EINVAL                      # Hq % Hkv
+    assert call(W=600) == EINVAL                     # W > N
+    assert call(B=0) == EINVAL
+    assert call(B=65, sl=a64([512] * 65)) == EINVAL  # more than 64 sequences
+    assert call(sl=a64([0])) == EINVAL
+    assert call(scale=float("nan")) == EINVAL
+    assert call(Hq=32, Hkv=2, W=128, sl=a64([4096])) == EINVAL  # G*W = 2048 > 512
+    assert call(q=None) == EALIGN
+    assert call(k=P + 8) == EALIGN
+    assert call(s=P + 2) == EALIGN
+    assert call(ws=None) == EWS
+    assert call(wsb=16) == EWS
+
+
+def test_refine_validation():
+    L = hk.lib()
+    sl = a64([1000])
+    ok = dict(s=P, B=1, sl=sl, L=1, Hkv=2, st=None, bi=None, pool=5, gamma=0.5, lo=0.8, hi=1.2,
+              r=0.1, z=P + (1 << 20), bo=None, ws=P + (1 << 24), wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.hubkv_refine(a["s"], a["B"], a["sl"], a["L"], a["Hkv"], a["st"], a["bi"],
+                              a["pool"], a["gamma"], a["lo"], a["hi"], a["r"], a["z"], a["bo"],
+                              a["ws"], a["wsb"], None)
+
+    assert call(pool=4) == EINVAL
+    assert call(pool=0) == EINVAL
+    assert call(pool=65) == EINVAL
+    assert call(gamma=0.0) == EINVAL
+    assert call(gamma=1.5) == EINVAL
+    assert call(lo=1.3) == EINVAL
+    assert call(r=-0.1) == EINVAL
+    assert call(r=1.5) == EINVAL
+    assert call(z=P) == EINVAL           # z aliases s
+    assert call(z=P + 400) == EINVAL     # overlapping ranges
+    assert call(s=None) == EALIGN
+    assert call(z=P + (1 << 20) + 2) == EALIGN
+    assert call(wsb=8) == EWS
+
+
+def test_select_validation():
+    L = hk.lib()
+    sl = a64([100, 50])
+
+    def call(kept, ns=4, nr=16, z=P, idx=P + 4096, B=2, s=sl):
+        return L.hubkv_select(z, B, s, 1, 2, a64(kept), ns, nr, idx, None)
+
+    assert call([10, 30]) == EINVAL    # fewer than the 20 protected tokens
+    assert call([30, 51]) == EINVAL    # more than the sequence
+    assert call([30, 30], ns=-1) == EINVAL
+    assert call([30, 30], z=None) == EALIGN
+    assert call([30, 30], idx=P + 2) == EALIGN
+
+
+def test_compact_validation():
+    L = hk.lib()
+    sl = a64([100])
+
+    def call(dt=1, d=128, kept=(10,), ki=P, ko=P + 65536):
+        return L.hubkv_compact(ki, P, dt, P, 1, sl, a64(list(kept)), 1, 2, d, ko, P + 131072, None)
+
+    assert call(dt=3) == EDTYPE
+    assert call(d=32) == EDTYPE
+    assert call(kept=(101,)) == EINVAL
+    assert call(kept=(-1,)) == EINVAL
+    assert call(ki=P + 8) == EALIGN
+    assert call(ko=None) == EALIGN
+
+
+def test_h2o_step_validation():
+    L = hk.lib()
+
+    def call(C_=64, ns=0, nr=8, Hq=4, Hkv=4, t=(100,), d=128, dt=1, acc=P, scale=0.1):
+        return L.h2o_step(P, P, P, dt, P, P, acc, P, a64(list(t)), len(t), Hq, Hkv, d, C_, ns, nr,
+                          scale, 0, None, None, None)
+
+    assert call(ns=60, nr=8) == EINVAL       # protected windows exceed the capacity
+    assert call(Hq=6) == EINVAL
+    assert call(Hq=64, Hkv=2) == EINVAL      # group of 32 query heads
+    assert call(C_=20000) == EINVAL          # logits do not fit the work-group
+    assert call(t=(-1,)) == EINVAL
+    assert call(d=80) == EDTYPE
+    assert call(dt=5) == EDTYPE
+    assert call(acc=P + 2) == EALIGN
+    assert call(scale=float("inf")) == EINVAL
+
+
+def test_python_binding_raises_on_missing_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(hk, "_lib", None)
+    monkeypatch.setattr(hk, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        hk.lib()

@@ -1,0 +1,317 @@
+"""GPU parity of the prefill path (score -> refine -> select -> compact)
+against the CPU oracle, through the C ABI.
+
+Bars (from the method's statement of the problem):
+  * given identical fp32 scores: refined scores, kept index sets and the
+    compacted K/V are bit-exact;
+  * scores within 1e-5 relative for fp32 inputs and 2e-2 relative for bf16
+    inputs with fp32 accumulation (observed far tighter, checked too);
+  * end to end on bf16, kept sets identical except for positions whose score
+    lies within that tolerance of the k-th boundary.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+from gpu_helpers import near_tie_sets_ok, note, rel_err, threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import token_scoring_top_amd as hk  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hk.lib()
+    oracle.set_threads(threads())
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    note(f"[gpu] {request.node.nodeid}")
+
+
+def _gpu_score(Q, K, seqlens, W, scale, causal, dtype):
+    s, st = hk.hubkv_score(to_dev(Q, dtype), to_dev(K, dtype), seqlens, W, scale, causal)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), st.cpu().numpy()
+
+
+# ------------------------------------------------------------------ score ---
+SCORE_CASES = [
+    # seqlens, L, Hq, Hkv, W, d, causal
+    ([300], 1, 2, 2, 16, 128, True),          # one ragged chunk, rows padded 16 -> 64
+    ([1500, 2100], 2, 4, 2, 24, 64, True),    # GQA, two layers, ragged batch, d = 64
+    ([2048], 1, 8, 2, 32, 128, False),        # 128 rows, no mask
+    ([5000], 1, 4, 1, 100, 128, True),        # 400 rows (7 row groups)
+    ([3000, 700, 1200], 1, 32, 8, 64, 128, True),  # 256 rows, three sequences
+    ([4100], 1, 4, 1, 128, 128, True),        # 512 rows, the largest group
+    ([64], 1, 1, 1, 64, 128, True),           # window covers the whole sequence
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: f"N{c[0]}-L{c[1]}-G{c[2]//c[3]}-W{c[4]}-d{c[5]}-c{int(c[6])}")
+def test_score_bf16_matches_oracle(case):
+    seqlens, L, Hq, Hkv, W, d, causal = case
+    rng = np.random.default_rng(sum(seqlens) + W)
+    T = sum(seqlens)
+    Q = S.round_bf16(rng.standard_normal((L, Hq, len(seqlens) * W, d), dtype=np.float32))
+    K = S.round_bf16(rng.standard_normal((L, Hkv, T, d), dtype=np.float32) * 1.5)
+    scale = 1 / math.sqrt(d)
+    s_o, st_o = oracle.score(Q, K, seqlens, W, scale, causal)
+    s_g, st_g = _gpu_score(Q, K, seqlens, W, scale, causal, "bf16")
+    err = rel_err(s_g, s_o, 1e-30)
+    assert err.max() < 2e-2
+    assert err.max() < 5e-5, f"max rel err {err.max():.3g}"  # fp32 accumulation of exact bf16 products
+    np.testing.assert_allclose(st_g[..., 0], st_o[..., 0], rtol=1e-5)
+    np.testing.assert_allclose(st_g[..., 1], st_o[..., 1], rtol=1e-4)
+
+
+@pytest.mark.parametrize("case", [([512], 1, 4, 4, 32, 64, True), ([700, 260], 2, 6, 2, 20, 128, True),
+                                  ([300], 1, 2, 1, 50, 64, False)])
+def test_score_f32_matches_oracle(case):
+    seqlens, L, Hq, Hkv, W, d, causal = case
+    rng = np.random.default_rng(7 + W)
+    T = sum(seqlens)
+    Q = rng.standard_normal((L, Hq, len(seqlens) * W, d), dtype=np.float32)
+    K = rng.standard_normal((L, Hkv, T, d), dtype=np.float32)
+    scale = 1 / math.sqrt(d)
+    s_o, st_o = oracle.score(Q, K, seqlens, W, scale, causal)
+    s_g, st_g = _gpu_score(Q, K, seqlens, W, scale, causal, "f32")
+    assert rel_err(s_g, s_o).max() < 1e-5
+    np.testing.assert_allclose(st_g[..., 0], st_o[..., 0], rtol=1e-6)
+
+
+def test_score_deterministic():
+    rng = np.random.default_rng(3)
+    Q = S.round_bf16(rng.standard_normal((1, 8, 64, 128), dtype=np.float32))
+    K = S.round_bf16(rng.standard_normal((1, 2, 5000, 128), dtype=np.float32))
+    a = _gpu_score(Q, K, [5000], 64, 0.088, True, "bf16")
+    b = _gpu_score(Q, K, [5000], 64, 0.088, True, "bf16")
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------- refine ---
+REFINE_CASES = [
+    ([1000], 1, 4, "attention", False, 5, 0.5, 0.2),
+    ([3000, 517, 9000], 2, 3, "attention", True, 5, 0.5, 0.1),
+    ([2049], 1, 2, "uniform", False, 3, 0.5, 1.0),
+    ([777, 1024], 1, 2, "attention", False, 7, 0.75, 0.05),
+    ([40000], 1, 2, "attention", True, 1, 0.5, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", REFINE_CASES, ids=lambda c: f"T{sum(c[0])}-{c[3]}-ties{int(c[4])}-p{c[5]}")
+def test_refine_bitexact_given_scores_and_beta(case):
+    seqlens, L, Hkv, kind, ties, pool, gamma, r = case
+    s = S.random_scores(seqlens, L, Hkv, seed=sum(seqlens), kind=kind, ties=ties)
+    beta = oracle.beta(oracle.head_stats(s, seqlens), seqlens)
+    z_o = oracle.refine(s, seqlens, beta, pool, gamma, r)
+    z_g, b_g = hk.hubkv_refine(to_dev(s, "f32"), seqlens, beta_in=to_dev(beta, "f32"), pool=pool,
+                               gamma=gamma, r=r)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(z_g.cpu().numpy(), z_o)
+    np.testing.assert_array_equal(b_g.cpu().numpy(), beta)
+
+
+@pytest.mark.parametrize("case", REFINE_CASES[:3], ids=lambda c: f"T{sum(c[0])}-{c[3]}")
+def test_refine_head_weight_from_scores(case):
+    # beta from statistics the GPU computes itself (and from given statistics)
+    seqlens, L, Hkv, kind, ties, pool, gamma, r = case
+    s = S.random_scores(seqlens, L, Hkv, seed=1 + sum(seqlens), kind=kind, ties=ties)
+    st = oracle.head_stats(s, seqlens)
+    beta = oracle.beta(st, seqlens)
+    z_o = oracle.refine(s, seqlens, beta, pool, gamma, r)
+    for stats_in in (None, torch.from_numpy(st).cuda()):
+        z_g, b_g = hk.hubkv_refine(to_dev(s, "f32"), seqlens, head_stats=stats_in, pool=pool,
+                                   gamma=gamma, r=r)
+        torch.cuda.synchronize()
+        b_g = b_g.cpu().numpy()
+        assert rel_err(b_g, beta).max() < 1e-6
+        assert rel_err(z_g.cpu().numpy(), z_o, 1e-30).max() < 1e-6
+
+
+# ----------------------------------------------------------------- select ---
+def _special_z(n, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.random(n).astype(np.float32)
+    k = max(1, n // 50)
+    z[rng.integers(0, n, k)] = np.nan
+    z[rng.integers(0, n, k)] = -0.0
+    z[rng.integers(0, n, k)] = 0.0
+    z[rng.integers(0, n, k)] = np.inf
+    z[rng.integers(0, n, k)] = -np.inf
+    z[rng.integers(0, n, k)] = -rng.random(k).astype(np.float32)
+    return z
+
+
+SELECT_CASES = [
+    # seqlens, L, Hkv, budget, n_sink, n_recent, kind
+    ([1000], 1, 2, 0.2, 0, 16, "attention"),
+    ([32768], 1, 4, 0.1, 4, 64, "attention"),
+    ([5000, 131, 20000], 2, 2, 0.1, 4, 64, "ties"),
+    ([70000], 1, 1, 0.05, 4, 128, "uniform"),
+    ([3000], 1, 2, 0.3, 2, 8, "special"),
+    ([200, 200], 1, 1, None, 4, 32, "attention"),     # kept == protected (StreamingLLM case)
+    ([200], 1, 1, 1.0, 4, 32, "attention"),           # keep everything
+    ([100], 1, 1, 0.5, 60, 60, "attention"),          # windows overlap: all protected
+    ([262144], 1, 1, 0.2, 4, 128, "ties"),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: f"T{sum(c[0])}-{c[6]}-b{c[3]}")
+def test_select_bitexact_given_scores(case):
+    seqlens, L, Hkv, budget, ns, nr, kind = case
+    if kind == "special":
+        z = np.stack([np.stack([_special_z(sum(seqlens), 10 * l + h) for h in range(Hkv)])
+                      for l in range(L)])
+    else:
+        z = S.random_scores(seqlens, L, Hkv, seed=len(seqlens) + sum(seqlens),
+                            kind="uniform" if kind == "uniform" else "attention",
+                            ties=(kind == "ties"))
+    if budget is None:
+        kept = np.array([oracle.protected_count(n, ns, nr) for n in seqlens])
+    else:
+        kept = np.maximum(S.budgets(seqlens, budget),
+                          [oracle.protected_count(n, ns, nr) for n in seqlens])
+    idx_o = oracle.select(z, seqlens, kept, ns, nr)
+    idx_g = hk.hubkv_select(to_dev(z, "f32"), seqlens, kept, ns, nr)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
+
+
+# ---------------------------------------------------------------- compact ---
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_compact_bitexact_given_indices(dtype, d):
+    seqlens = [3000, 517, 1200]
+    L, Hkv = 2, 3
+    T = sum(seqlens)
+    rng = np.random.default_rng(d)
+    K = rng.standard_normal((L, Hkv, T, d), dtype=np.float32)
+    V = rng.standard_normal((L, Hkv, T, d), dtype=np.float32)
+    if dtype == "bf16":
+        K, V = S.round_bf16(K), S.round_bf16(V)
+    z = S.random_scores(seqlens, L, Hkv, seed=5)
+    kept = S.budgets(seqlens, 0.15)
+    idx = oracle.select(z, seqlens, kept, 4, 32)
+    ko, vo = oracle.compact(K, V, idx, seqlens, kept)
+    kg, vg = hk.hubkv_compact(to_dev(K, dtype), to_dev(V, dtype),
+                              torch.from_numpy(idx).cuda(), seqlens, kept)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(kg), ko)
+    np.testing.assert_array_equal(to_host(vg), vo)
+
+
+# ------------------------------------------------------------ whole chain ---
+def _gpu_chain(Q, K, V, w, budget=None, r=None):
+    kept = w.kept(budget)
+    Qd, Kd, Vd = to_dev(Q, w.dtype), to_dev(K, w.dtype), to_dev(V, w.dtype)
+    s, st = hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal)
+    z, beta = hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                              beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r if r is None else r)
+    idx = hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent)
+    ko, vo = hk.hubkv_compact(Kd, Vd, idx, w.seqlens, kept)
+    torch.cuda.synchronize()
+    return dict(s=s.cpu().numpy(), stats=st.cpu().numpy(), beta=beta.cpu().numpy(),
+                z=z.cpu().numpy(), idx=idx.cpu().numpy(), k_out=to_host(ko), v_out=to_host(vo),
+                kept=kept)
+
+
+def _check_chain(g, o, K, V, w, tol_s, tol_set, check_sets_exact=False):
+    assert rel_err(g["s"], o["s"]).max() < tol_s
+    assert rel_err(g["beta"], o["beta"]).max() < 1e-4
+    ok, nd = near_tie_sets_ok(g["idx"], o["idx"], o["z"], w.seqlens, g["kept"], w.n_sink,
+                              w.n_recent, tol_set)
+    assert ok, f"kept sets differ beyond near-ties ({nd} positions)"
+    if check_sets_exact:
+        np.testing.assert_array_equal(g["idx"], o["idx"])
+    # compaction of the GPU's own kept set: rows must be those of the input
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)])
+    ko = np.concatenate([[0], np.cumsum(g["kept"])])
+    for l in range(K.shape[0]):
+        for h in range(K.shape[1]):
+            for b in range(len(w.seqlens)):
+                rows = g["idx"][l, h, ko[b]:ko[b + 1]] + cu[b]
+                np.testing.assert_array_equal(g["k_out"][l, h, ko[b]:ko[b + 1]], K[l, h][rows])
+                np.testing.assert_array_equal(g["v_out"][l, h, ko[b]:ko[b + 1]], V[l, h][rows])
+
+
+def test_chain_tiny_fp32_workload():
+    w = S.workload(1)
+    Q, K, V = S.prefill_inputs(w)
+    o = oracle.prefill_chain(Q, K, V, w)
+    g = _gpu_chain(Q, K, V, w)
+    _check_chain(g, o, K, V, w, tol_s=1e-5, tol_set=1e-5)
+
+
+def test_chain_llama2_7b_layer_workload():
+    w = S.workload(2)
+    note("  generating 32 heads x 32768 tokens (bf16)")
+    Q, K, V = S.prefill_inputs(w, threads=threads())
+    note("  oracle chain")
+    o = oracle.prefill_chain(Q, K, V, w)
+    note("  gpu chain")
+    g = _gpu_chain(Q, K, V, w)
+    _check_chain(g, o, K, V, w, tol_s=2e-2, tol_set=2e-2)
+    assert rel_err(g["s"], o["s"]).max() < 5e-5
+
+
+def test_chain_gqa_long_context_two_layers():
+    # 131072 tokens, 8 KV heads x 4 query heads; layers 0 and 1 of the 32-layer
+    # workload run on the GPU together, the oracle checks layer 0 in full
+    w = S.workload(3).with_(L=2)
+    note("  generating 2 layers x 8 heads x 131072 tokens")
+    Q, K, V = S.prefill_inputs(w, threads=threads())
+    g = _gpu_chain(Q, K, V, w)
+    w0 = w.with_(L=1)
+    note("  oracle chain on layer 0")
+    o = oracle.prefill_chain(Q[:1], K[:1], V[:1], w0)
+    g0 = {k: (v[:1] if k not in ("kept",) else v) for k, v in g.items()}
+    _check_chain(g0, o, K[:1], V[:1], w0, tol_s=2e-2, tol_set=2e-2)
+    assert rel_err(g0["s"], o["s"]).max() < 5e-5
+    # layer 1: invariants that hold at any size
+    G = w.G
+    np.testing.assert_allclose(g["s"][1].astype(np.float64).sum(-1), G * w.W, rtol=1e-4)
+    assert (g["beta"][1] >= np.float32(0.8)).all() and (g["beta"][1] <= np.float32(1.2)).all()
+
+
+@pytest.mark.parametrize("budget", [0.05, 0.1, 0.2])
+def test_chain_ragged_batch_at_scale(budget):
+    # 4 sequences of 64K..512K tokens on the GPU; the oracle checks the 64K
+    # sequence in full (its 8 heads), the rest by invariants
+    w = S.workload(5).with_(budget=budget, r=budget)
+    key = "c5"
+    cache = test_chain_ragged_batch_at_scale.__dict__
+    if key not in cache:
+        note("  generating 4 sequences (983040 tokens) x 8 heads")
+        cache[key] = S.prefill_inputs(w, threads=threads())
+    Q, K, V = cache[key]
+    g = _gpu_chain(Q, K, V, w)
+    w0 = w.with_(seqlens=(w.seqlens[0],))
+    n0 = w.seqlens[0]
+    note("  oracle chain on the 65536-token sequence")
+    o = oracle.prefill_chain(np.ascontiguousarray(Q[:, :, :w.W]), np.ascontiguousarray(K[:, :, :n0]),
+                             np.ascontiguousarray(V[:, :, :n0]), w0)
+    k0 = int(w.kept()[0])
+    g0 = dict(s=g["s"][:, :, :n0], beta=g["beta"][:, :1], idx=g["idx"][:, :, :k0],
+              k_out=g["k_out"][:, :, :k0], v_out=g["v_out"][:, :, :k0], kept=g["kept"][:1])
+    _check_chain(g0, o, K[:, :, :n0], V[:, :, :n0], w0, tol_s=2e-2, tol_set=2e-2)
+    assert rel_err(g0["s"], o["s"]).max() < 5e-5
+    # every sequence: column sums, kept counts, ascending, protected windows
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)])
+    ko = np.concatenate([[0], np.cumsum(g["kept"])])
+    for b, N in enumerate(w.seqlens):
+        np.testing.assert_allclose(g["s"][0, :, cu[b]:cu[b + 1]].astype(np.float64).sum(-1),
+                                   w.G * w.W, rtol=1e-4)
+        for h in range(w.Hkv):
+            x = g["idx"][0, h, ko[b]:ko[b + 1]]
+            assert (np.diff(x) > 0).all() and x[0] == 0 and x[-1] == N - 1
+            assert set(range(w.n_sink)) <= set(x[:w.n_sink + 1].tolist())
+            assert (x[-w.n_recent:] == np.arange(N - w.n_recent, N)).all()

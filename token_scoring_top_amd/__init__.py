@@ -1,0 +1,238 @@
+"""token_scoring_top_amd -- MI355X (gfx950) KV-cache retention scoring and Top-K.
+
+Thin Python binding of libhubkv.so (include/hubkv.h).  It only marshals
+arguments: torch tensors become device pointers, the current torch stream
+becomes the HIP stream, and outputs/workspaces are allocated with torch.
+Every step of the path runs in the library's HIP kernels; there is no
+fallback, and importing the binding without the built library raises.
+
+Functions (names follow the C ABI):
+    hubkv_score(q, k, seqlens, W, scale, causal=True) -> (s, head_stats)
+    hubkv_refine(s, seqlens, ...)                      -> (z, beta)
+    hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
+    hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
+    h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, ...) -> evicted
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhubkv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "hubkv.h")
+
+HUBKV_F32, HUBKV_BF16 = 0, 1
+STATUS = {0: "HUBKV_OK", -1: "HUBKV_EINVAL", -2: "HUBKV_EDTYPE", -3: "HUBKV_EALIGN",
+          -4: "HUBKV_EWORKSPACE", -5: "HUBKV_EHIP"}
+
+
+class HubkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip: int = 0):
+        self.status = status
+        msg = f"{fn} failed: {STATUS.get(status, status)}"
+        if status == -5:
+            msg += f" (hipError {hip})"
+        super().__init__(msg)
+
+
+_lib = None
+_vp, _i, _i64, _f, _sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+_i64p = C.POINTER(C.c_int64)
+
+_SIGS = {
+    "hubkv_score_workspace": (_sz, [_i, _i64p, _i, _i, _i, _i, _i, _i]),
+    "hubkv_score": (_i, [_vp, _vp, _i, _i, _i64p, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz,
+                         _vp]),
+    "hubkv_refine_workspace": (_sz, [_i, _i64p, _i, _i]),
+    "hubkv_refine": (_i, [_vp, _i, _i64p, _i, _i, _vp, _vp, _i, _f, _f, _f, _f, _vp, _vp, _vp, _sz,
+                          _vp]),
+    "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp]),
+    "hubkv_compact": (_i, [_vp, _vp, _i, _vp, _i, _i64p, _i64p, _i, _i, _i, _vp, _vp, _vp]),
+    "h2o_step": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, _i, _f,
+                      _i, _vp, _vp, _vp]),
+    "hubkv_protected_count": (_i64, [_i64, _i, _i]),
+    "hubkv_strerror": (C.c_char_p, [_i]),
+    "hubkv_last_hip_error": (_i, []),
+    "hubkv_version": (_i, []),
+}
+
+
+def lib():
+    """The loaded libhubkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m token_scoring_top_amd.build` (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/hubkv.h declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def _arr64(xs) -> C.Array:
+    xs = [int(x) for x in xs]
+    return (C.c_int64 * len(xs))(*xs)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise HubkvError(fn, rc, lib().hubkv_last_hip_error() if rc == -5 else 0)
+
+
+# -------------------------------------------------------------------------
+# torch helpers (torch is only used for device memory and streams)
+# -------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return HUBKV_F32
+    if t.dtype == torch.bfloat16:
+        return HUBKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# -------------------------------------------------------------------------
+# Entry points
+# -------------------------------------------------------------------------
+def hubkv_score(q, k, seqlens: Sequence[int], W: int, scale: float, causal: bool = True,
+                s=None, head_stats=None, workspace=None, stream=None):
+    """q [L][Hq][B*W][d], k [L][Hkv][T][d] (fp32 or bf16) -> s fp32 [L][Hkv][T],
+    head_stats fp64 [L][B][Hkv][2]."""
+    torch = _torch()
+    L, Hq, BW, d = q.shape
+    L2, Hkv, T, d2 = k.shape
+    B = len(seqlens)
+    if L2 != L or d2 != d or BW != B * W or T != sum(seqlens) or q.dtype != k.dtype:
+        raise ValueError("inconsistent q/k shapes")
+    sl = _arr64(seqlens)
+    dt = _dtype_code(q)
+    if s is None:
+        s = torch.empty((L, Hkv, T), dtype=torch.float32, device=q.device)
+    if head_stats is None:
+        head_stats = torch.empty((L, B, Hkv, 2), dtype=torch.float64, device=q.device)
+    nb = lib().hubkv_score_workspace(B, sl, L, Hq, Hkv, W, d, dt)
+    if workspace is None:
+        workspace = _workspace(nb, q.device)
+    _check("hubkv_score", lib().hubkv_score(_ptr(q), _ptr(k), dt, B, sl, L, Hq, Hkv, W, d,
+                                            float(scale), int(bool(causal)), _ptr(s),
+                                            _ptr(head_stats), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)))
+    return s, head_stats
+
+
+def hubkv_refine(s, seqlens: Sequence[int], head_stats=None, beta_in=None, pool: int = 5,
+                 gamma: float = 0.5, beta_lo: float = 0.8, beta_hi: float = 1.2, r: float = 0.1,
+                 z=None, beta_out=None, workspace=None, stream=None):
+    """s fp32 [L][Hkv][T] -> z fp32 [L][Hkv][T], beta fp32 [L][B][Hkv]."""
+    torch = _torch()
+    L, Hkv, T = s.shape
+    B = len(seqlens)
+    sl = _arr64(seqlens)
+    if z is None:
+        z = torch.empty_like(s)
+    if beta_out is None:
+        beta_out = torch.empty((L, B, Hkv), dtype=torch.float32, device=s.device)
+    nb = lib().hubkv_refine_workspace(B, sl, L, Hkv)
+    if workspace is None:
+        workspace = _workspace(nb, s.device)
+    _check("hubkv_refine", lib().hubkv_refine(_ptr(s), B, sl, L, Hkv, _ptr(head_stats),
+                                              _ptr(beta_in), int(pool), float(gamma),
+                                              float(beta_lo), float(beta_hi), float(r), _ptr(z),
+                                              _ptr(beta_out), _ptr(workspace), workspace.numel(),
+                                              _stream(stream)))
+    return z, beta_out
+
+
+def hubkv_select(z, seqlens: Sequence[int], kept: Sequence[int], n_sink: int, n_recent: int,
+                 idx=None, stream=None):
+    """z fp32 [L][Hkv][T] -> idx int32 [L][Hkv][sum kept] (ascending per sequence)."""
+    torch = _torch()
+    L, Hkv, T = z.shape
+    B = len(seqlens)
+    if idx is None:
+        idx = torch.empty((L, Hkv, int(sum(kept))), dtype=torch.int32, device=z.device)
+    _check("hubkv_select", lib().hubkv_select(_ptr(z), B, _arr64(seqlens), L, Hkv, _arr64(kept),
+                                              int(n_sink), int(n_recent), _ptr(idx),
+                                              _stream(stream)))
+    return idx
+
+
+def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], k_out=None,
+                  v_out=None, stream=None):
+    """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [L][Hkv][sum kept][d]."""
+    torch = _torch()
+    L, Hkv, T, d = k_in.shape
+    K = int(sum(kept))
+    if k_out is None:
+        k_out = torch.empty((L, Hkv, K, d), dtype=k_in.dtype, device=k_in.device)
+    if v_out is None:
+        v_out = torch.empty((L, Hkv, K, d), dtype=v_in.dtype, device=v_in.device)
+    _check("hubkv_compact", lib().hubkv_compact(_ptr(k_in), _ptr(v_in), _dtype_code(k_in),
+                                                _ptr(idx), len(seqlens), _arr64(seqlens),
+                                                _arr64(kept), L, Hkv, d, _ptr(k_out), _ptr(v_out),
+                                                _stream(stream)))
+    return k_out, v_out
+
+
+def h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, scale: float, n_sink: int = 0,
+             n_recent: int = 0, include_self: bool = False, evicted=None, probs=None,
+             stream=None):
+    """One H2O decode step, in place on (k_cache, v_cache, acc, pos).
+    q [B][Hq][d], k_new/v_new [B][Hkv][d], caches [B][Hkv][C][d], acc/pos
+    [B][Hkv][C]; t: int or per-sequence list.  Returns evicted int32 [B][Hkv]."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, Cs, _ = k_cache.shape
+    tt = [int(t)] * B if isinstance(t, int) else [int(x) for x in t]
+    if evicted is None:
+        evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    _check("h2o_step", lib().h2o_step(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q),
+                                      _ptr(k_cache), _ptr(v_cache), _ptr(acc), _ptr(pos),
+                                      _arr64(tt), B, Hq, Hkv, d, Cs, int(n_sink), int(n_recent),
+                                      float(scale), int(bool(include_self)), _ptr(evicted),
+                                      _ptr(probs), _stream(stream)))
+    return evicted
+
+
+def protected_count(N: int, n_sink: int, n_recent: int) -> int:
+    return int(lib().hubkv_protected_count(int(N), int(n_sink), int(n_recent)))

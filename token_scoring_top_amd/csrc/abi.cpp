@@ -1,0 +1,245 @@
+// abi.cpp -- the C ABI declared in include/hubkv.h: host-side validation,
+// workspace sizing and dispatch to the gfx950 kernels.
+//
+// Every entry point validates all of its arguments with plain host code
+// before it makes any HIP call, so a rejected call enqueues nothing and
+// leaves the outputs untouched.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/hubkv.h"
+#include "internal.hpp"
+
+using namespace hubkv;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return HUBKV_OK;
+  g_last_hip_error = (int)e;
+  return HUBKV_EHIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;  // positions are int32
+
+// Validate the sequence table and fill it; tile size `tile` sets tile_off.
+int make_table(SeqTable& st, int B, const int64_t* seqlens, int tile) {
+  if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
+  memset(&st, 0, sizeof(st));
+  st.B = B;
+  st.tile = tile;
+  int64_t cu = 0, tiles = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = seqlens[b];
+    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    st.N[b] = n;
+    st.cu[b] = cu;
+    st.tile_off[b] = (int32_t)tiles;
+    cu += n;
+    tiles += (n + tile - 1) / tile;
+    if (cu >= ((int64_t)1 << 40) || tiles >= ((int64_t)1 << 30)) return HUBKV_EINVAL;
+  }
+  st.tile_off[B] = (int32_t)tiles;
+  return HUBKV_OK;
+}
+
+int check_kept(SeqTable& st, const int64_t* kept, int n_sink, int n_recent, bool need_protected) {
+  if (!kept || n_sink < 0 || n_recent < 0) return HUBKV_EINVAL;
+  int64_t ko = 0;
+  for (int b = 0; b < st.B; ++b) {
+    const int64_t P = need_protected ? hubkv_protected_count(st.N[b], n_sink, n_recent) : 0;
+    if (kept[b] < P || kept[b] > st.N[b]) return HUBKV_EINVAL;
+    st.ko[b] = ko;
+    st.kept[b] = kept[b];
+    ko += kept[b];
+  }
+  if (ko >= kMaxTokens) return HUBKV_EINVAL;
+  return HUBKV_OK;
+}
+
+int check_dtype_d(int dtype, int d) {
+  if (dtype != HUBKV_F32 && dtype != HUBKV_BF16) return HUBKV_EDTYPE;
+  if (d != 64 && d != 128) return HUBKV_EDTYPE;
+  return HUBKV_OK;
+}
+
+int check_score_shape(int L, int Hq, int Hkv, int W, const SeqTable& st) {
+  if (L < 1 || Hq < 1 || Hkv < 1 || W < 1 || Hq % Hkv) return HUBKV_EINVAL;
+  if ((int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if ((int64_t)(Hq / Hkv) * W > 512) return HUBKV_EINVAL;
+  for (int b = 0; b < st.B; ++b)
+    if (st.N[b] < W) return HUBKV_EINVAL;
+  return HUBKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hubkv_protected_count(int64_t N, int n_sink, int n_recent) {
+  if (N <= 0) return 0;
+  const int64_t a = n_sink < N ? (n_sink > 0 ? n_sink : 0) : N;
+  int64_t c = N - (n_recent > 0 ? n_recent : 0);
+  if (c < 0) c = 0;
+  if (c <= a) return N;
+  return a + (N - c);
+}
+
+const char* hubkv_strerror(int status) {
+  switch (status) {
+    case HUBKV_OK: return "success";
+    case HUBKV_EINVAL: return "invalid size, count or parameter";
+    case HUBKV_EDTYPE: return "unsupported element type or head dimension";
+    case HUBKV_EALIGN: return "null or misaligned pointer";
+    case HUBKV_EWORKSPACE: return "workspace missing or too small";
+    case HUBKV_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int hubkv_last_hip_error(void) { return g_last_hip_error; }
+
+int hubkv_version(void) { return 100; }
+
+size_t hubkv_score_workspace(int B, const int64_t* seqlens, int L, int Hq, int Hkv, int W, int d,
+                             int dtype) {
+  if (check_dtype_d(dtype, d) != HUBKV_OK) return 0;
+  SeqTable st;
+  const int chunk = dtype == HUBKV_BF16 ? kScoreChunkMfma : kScoreChunkF32;
+  if (make_table(st, B, seqlens, chunk) != HUBKV_OK) return 0;
+  if (check_score_shape(L, Hq, Hkv, W, st) != HUBKV_OK) return 0;
+  return score_geometry(st, L, Hq, Hkv, W, d, dtype).bytes;
+}
+
+int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens, int L,
+                int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                double* head_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  SeqTable st;
+  const int chunk = dtype == HUBKV_BF16 ? kScoreChunkMfma : kScoreChunkF32;
+  if ((rc = make_table(st, B, seqlens, chunk))) return rc;
+  if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
+  if (!isfinite(scale)) return HUBKV_EINVAL;
+  if (!q || !k || !s || !aligned(q, 16) || !aligned(k, 16) || !aligned(s, 4)) return HUBKV_EALIGN;
+  if (head_stats && !aligned(head_stats, 8)) return HUBKV_EALIGN;
+  const ScoreGeom geo = score_geometry(st, L, Hq, Hkv, W, d, dtype);
+  if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
+  if (!aligned(workspace, 256)) return HUBKV_EALIGN;
+  return hip_status(launch_score(q, k, dtype, st, L, Hq, Hkv, W, d, scale, causal, s, head_stats,
+                                 (char*)workspace, geo, (hipStream_t)stream));
+}
+
+size_t hubkv_refine_workspace(int B, const int64_t* seqlens, int L, int Hkv) {
+  SeqTable st;
+  if (make_table(st, B, seqlens, kRefineTile) != HUBKV_OK) return 0;
+  if (L < 1 || Hkv < 1 || Hkv > 1024 || (int64_t)L * Hkv > kMaxGridY) return 0;
+  return refine_geometry(st, L, Hkv).bytes;
+}
+
+int hubkv_refine(const float* s, int B, const int64_t* seqlens, int L, int Hkv,
+                 const double* head_stats, const float* beta_in, int pool, float gamma,
+                 float beta_lo, float beta_hi, float r, float* z, float* beta_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  SeqTable st;
+  int rc = make_table(st, B, seqlens, kRefineTile);
+  if (rc) return rc;
+  if (L < 1 || Hkv < 1 || Hkv > 1024 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if (pool < 1 || pool % 2 == 0 || pool > 63) return HUBKV_EINVAL;
+  if (!(gamma > 0.f && gamma <= 1.f)) return HUBKV_EINVAL;
+  if (!(isfinite(beta_lo) && isfinite(beta_hi) && beta_lo <= beta_hi)) return HUBKV_EINVAL;
+  if (!(r >= 0.f && r <= 1.f)) return HUBKV_EINVAL;
+  if (!s || !z || !aligned(s, 4) || !aligned(z, 4)) return HUBKV_EALIGN;
+  if ((head_stats && !aligned(head_stats, 8)) || (beta_in && !aligned(beta_in, 4)) ||
+      (beta_out && !aligned(beta_out, 4)))
+    return HUBKV_EALIGN;
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) T += st.N[b];
+  const uintptr_t n = (uintptr_t)((int64_t)L * Hkv * T) * sizeof(float);
+  if ((uintptr_t)s < (uintptr_t)z + n && (uintptr_t)z < (uintptr_t)s + n) return HUBKV_EINVAL;
+  const RefineGeom geo = refine_geometry(st, L, Hkv);
+  if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
+  if (!aligned(workspace, 256)) return HUBKV_EALIGN;
+  char* ws = (char*)workspace;
+  hipStream_t strm = (hipStream_t)stream;
+  const double* stats = head_stats;
+  if (!beta_in && !stats) {
+    double* st_ws = (double*)(ws + geo.off_stats);
+    rc = hip_status(launch_head_stats(s, st, L, Hkv, (double*)(ws + geo.off_part), st_ws, strm));
+    if (rc) return rc;
+    stats = st_ws;
+  }
+  const float r2 = r * r;  // fp32 product, as the gate formula is evaluated in fp32
+  return hip_status(launch_refine(s, st, L, Hkv, stats, beta_in, pool, gamma, beta_lo, beta_hi, r2,
+                                  z, beta_out, (float*)(ws + geo.off_beta), strm));
+}
+
+int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
+                 const int64_t* kept, int n_sink, int n_recent, int32_t* idx, void* stream) {
+  SeqTable st;
+  int rc = make_table(st, B, seqlens, kRefineTile);
+  if (rc) return rc;
+  if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if ((rc = check_kept(st, kept, n_sink, n_recent, true))) return rc;
+  if (!z || !idx || !aligned(z, 4) || !aligned(idx, 4)) return HUBKV_EALIGN;
+  return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, (hipStream_t)stream));
+}
+
+int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
+                  const int64_t* seqlens, const int64_t* kept, int L, int Hkv, int d, void* k_out,
+                  void* v_out, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  SeqTable st;
+  if ((rc = make_table(st, B, seqlens, kRefineTile))) return rc;
+  if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if ((rc = check_kept(st, kept, 0, 0, false))) return rc;
+  if (!k_in || !v_in || !k_out || !v_out || !idx) return HUBKV_EALIGN;
+  if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      !aligned(idx, 4))
+    return HUBKV_EALIGN;
+  return hip_status(launch_compact(k_in, v_in, dtype == HUBKV_BF16 ? 2 : 4, idx, st, L, Hkv, d,
+                                   k_out, v_out, (hipStream_t)stream));
+}
+
+int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+             void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
+             int d, int C, int n_sink, int n_recent, float scale, int include_self,
+             int32_t* evicted, float* probs, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
+  const int G = Hq / Hkv;
+  if (G > 16 || C < 1 || (int64_t)G * C > 12288) return HUBKV_EINVAL;
+  if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > C) return HUBKV_EINVAL;
+  if ((int64_t)B * Hkv > ((int64_t)1 << 30) || !isfinite(scale)) return HUBKV_EINVAL;
+  H2OArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int b = 0; b < B; ++b) {
+    if (t[b] < 0 || t[b] >= kMaxTokens - 1) return HUBKV_EINVAL;
+    a.t[b] = t[b];
+  }
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !acc || !pos) return HUBKV_EALIGN;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(acc, 4) || !aligned(pos, 4))
+    return HUBKV_EALIGN;
+  if ((evicted && !aligned(evicted, 4)) || (probs && !aligned(probs, 4))) return HUBKV_EALIGN;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.C = C;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.include_self = include_self ? 1 : 0;
+  a.scale = scale;
+  return hip_status(launch_h2o_step(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, a, evicted,
+                                    probs, (hipStream_t)stream));
+}
+
+}  // extern "C"

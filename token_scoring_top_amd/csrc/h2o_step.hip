@@ -1,0 +1,267 @@
+// h2o_step.hip -- one decode step of H2O greedy eviction on fixed cache slots.
+//
+// H2O breakdown page: "greedy eviction" (the current query's softmax over the
+// cached tokens is added to their accumulated scores, the new token enters
+// with score 0, and over budget the lowest accumulated score is evicted), the
+// heavy + recent section (a recent window is protected from eviction), the
+// per-head section (each head evicts independently) and the FlexGen section
+// (slots are preallocated; the evicted slot is overwritten by the new token,
+// and the score update rides on the attention pass).
+//
+// One work-group per (sequence, KV head).  Waves sweep the slots, a group of
+// lanes per slot row: each lane loads 16 bytes of the row and the partial dot
+// products are folded with shuffles; the logits of the group's query heads
+// stay in LDS.  After block-wide softmax statistics, each thread updates the
+// scores of the slots it owns and tracks the eviction candidate with the
+// smallest (score, position); a block reduction picks the slot to overwrite.
+#include "internal.hpp"
+
+namespace hubkv {
+
+namespace {
+
+constexpr int kH2OThreads = 256;
+constexpr int kMaxG = 16;
+constexpr float kLog2eH = 1.4426950408889634f;
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x);
+template <>
+__device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f<__bf16>(__bf16 x) { return (float)x; }
+
+__device__ __forceinline__ uint32_t asc_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    T* __restrict__ k_cache, T* __restrict__ v_cache, float* __restrict__ acc,
+    int32_t* __restrict__ pos, H2OArgs a, int32_t* __restrict__ evicted,
+    float* __restrict__ probs) {
+  constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane piece
+  constexpr int LPR = D / EPL;              // lanes per slot row
+  constexpr int RPW = 64 / LPR;             // rows per wave per sweep step
+  constexpr int WAVES = kH2OThreads / 64;
+  extern __shared__ float lg[];  // [G][C] logits in log2 units
+  __shared__ float qs[kMaxG][D];
+  __shared__ float red[WAVES][kMaxG];
+  __shared__ float Mh[kMaxG], iLh[kMaxG], selfx[kMaxG];
+  __shared__ unsigned long long cand_key[WAVES];
+  __shared__ int cand_slot[WAVES], empty_w[WAVES];
+  __shared__ int dec_slot;
+  __shared__ float dec_acc;
+
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv, g = u % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int C = a.C;
+  const int64_t t = a.t[b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float c2 = a.scale * kLog2eH;
+
+  for (int i = tid; i < G * D; i += kH2OThreads)
+    qs[i / D][i % D] = to_f<T>(q[((int64_t)b * a.Hq + g * G + i / D) * D + i % D]);
+  __syncthreads();
+
+  // ---- logits over the occupied slots
+  const T* Kc = k_cache + (int64_t)u * C * D;
+  const int32_t* P = pos + (int64_t)u * C;
+  float* A = acc + (int64_t)u * C;
+  const int piece = lane % LPR, rsub = lane / LPR;
+  for (int j0 = wave * RPW; j0 < C; j0 += WAVES * RPW) {
+    const int j = j0 + rsub;
+    float kv[EPL];
+    const bool have = j < C;
+    if (have) {
+      const u32x4 raw = *(const u32x4*)(Kc + (int64_t)j * D + piece * EPL);
+      const T* e = (const T*)&raw;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) kv[x] = to_f<T>(e[x]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) kv[x] = 0.f;
+    }
+    const bool occ = have && P[j] >= 0;
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+      if (piece == 0 && have) lg[h * C + j] = occ ? d * c2 : -INFINITY;
+    }
+  }
+  if (tid < G) {
+    float d = -INFINITY;
+    if (a.include_self) {
+      d = 0.f;
+      const T* kn = k_new + ((int64_t)b * a.Hkv + g) * D;
+      for (int x = 0; x < D; ++x) d = fmaf(qs[tid][x], to_f<T>(kn[x]), d);
+      d *= c2;
+    }
+    selfx[tid] = d;
+  }
+  __syncthreads();
+
+  // ---- softmax statistics per query head
+  for (int h = 0; h < G; ++h) {
+    float m = -INFINITY;
+    for (int j = tid; j < C; j += kH2OThreads) m = fmaxf(m, lg[h * C + j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red[wave][h] = m;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = selfx[tid];
+    for (int w = 0; w < WAVES; ++w) m = fmaxf(m, red[w][tid]);
+    Mh[tid] = m;
+  }
+  __syncthreads();
+  for (int h = 0; h < G; ++h) {
+    const float m = Mh[h];
+    float s = 0.f;
+    if (m > -INFINITY)
+      for (int j = tid; j < C; j += kH2OThreads) s += __builtin_amdgcn_exp2f(lg[h * C + j] - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) red[wave][h] = s;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const float m = Mh[tid];
+    float s = (m > -INFINITY && selfx[tid] > -INFINITY) ? __builtin_amdgcn_exp2f(selfx[tid] - m) : 0.f;
+    for (int w = 0; w < WAVES; ++w) s += red[w][tid];
+    iLh[tid] = s > 0.f ? 1.f / s : 0.f;
+  }
+  __syncthreads();
+
+  // ---- score update, eviction candidate, first empty slot
+  const int64_t lo = a.n_sink, hi = t - a.n_recent;
+  unsigned long long best = ~0ull;
+  int best_slot = -1, first_empty = 0x7fffffff;
+  for (int j = tid; j < C; j += kH2OThreads) {
+    const int32_t pj = P[j];
+    float add = 0.f;
+    for (int h = 0; h < G; ++h) {
+      const float p = pj >= 0 ? __builtin_amdgcn_exp2f(lg[h * C + j] - Mh[h]) * iLh[h] : 0.f;
+      add += p;
+      if (probs) probs[((int64_t)b * a.Hq + g * G + h) * (C + 1) + j] = p;
+    }
+    if (pj < 0) {
+      first_empty = min(first_empty, j);
+    } else {
+      const float na = A[j] + add;
+      A[j] = na;
+      if (pj >= lo && pj <= hi) {
+        const unsigned long long key = ((unsigned long long)asc_key(na) << 32) | (uint32_t)pj;
+        if (key < best) {
+          best = key;
+          best_slot = j;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long ok = __shfl_xor(best, off);
+    const int os = __shfl_xor(best_slot, off);
+    if (ok < best) {
+      best = ok;
+      best_slot = os;
+    }
+    first_empty = min(first_empty, __shfl_xor(first_empty, off));
+  }
+  if (lane == 0) {
+    cand_key[wave] = best;
+    cand_slot[wave] = best_slot;
+    empty_w[wave] = first_empty;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float self_acc = 0.f;
+    for (int h = 0; h < G; ++h) {
+      const float p = (Mh[h] > -INFINITY && selfx[h] > -INFINITY)
+                          ? __builtin_amdgcn_exp2f(selfx[h] - Mh[h]) * iLh[h] : 0.f;
+      self_acc += p;
+      if (probs) probs[((int64_t)b * a.Hq + g * G + h) * (C + 1) + C] = p;
+    }
+    unsigned long long bk = ~0ull;
+    int bs = -1, fe = 0x7fffffff;
+    for (int w = 0; w < WAVES; ++w) {
+      if (cand_key[w] < bk) {
+        bk = cand_key[w];
+        bs = cand_slot[w];
+      }
+      fe = min(fe, empty_w[w]);
+    }
+    int slot = -1, ev = -1;
+    if (fe < C) {
+      slot = fe;
+    } else {
+      // the new token competes when it is outside both protected windows
+      if (t >= lo && t <= hi) {
+        const unsigned long long nk = ((unsigned long long)asc_key(self_acc) << 32) | (uint32_t)t;
+        if (nk < bk) {
+          bk = nk;
+          bs = -2;
+        }
+      }
+      if (bs == -2) {
+        ev = (int)t;
+      } else if (bs >= 0) {
+        slot = bs;
+        ev = (int)(bk & 0xffffffffu);
+      }
+    }
+    dec_slot = slot;
+    dec_acc = self_acc;  // 0 unless the new token attends to itself
+    if (evicted) evicted[u] = ev;
+  }
+  __syncthreads();
+  const int slot = dec_slot;
+  if (slot >= 0) {
+    // the slot's owner thread rewrites its score and position (it wrote the
+    // updated score above, so program order keeps the final value)
+    if ((slot % kH2OThreads) == tid) {
+      A[slot] = dec_acc;
+      pos[(int64_t)u * C + slot] = (int32_t)t;
+    }
+    if (wave == 0 && lane < LPR) {
+      const int64_t src = ((int64_t)b * a.Hkv + g) * D + lane * EPL;
+      const int64_t dst = ((int64_t)u * C + slot) * D + lane * EPL;
+      *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_new + src);
+      *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_new + src);
+    }
+  }
+}
+
+}  // namespace
+
+size_t h2o_lds_bytes(int G, int C) { return (size_t)G * C * sizeof(float); }
+
+hipError_t launch_h2o_step(const void* q, const void* k_new, const void* v_new, int dtype,
+                           void* k_cache, void* v_cache, float* acc, int32_t* pos,
+                           const H2OArgs& a, int32_t* evicted, float* probs, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const size_t lds = h2o_lds_bytes(G, a.C);
+  const dim3 grid(a.B * a.Hkv), block(kH2OThreads);
+#define H2O_LAUNCH(T, D)                                                                        \
+  hipLaunchKernelGGL((h2o_step_kernel<T, D>), grid, block, lds, stream, (const T*)q,            \
+                     (const T*)k_new, (const T*)v_new, (T*)k_cache, (T*)v_cache, acc, pos, a,   \
+                     evicted, probs)
+  if (dtype == 1) {
+    if (a.d == 128) H2O_LAUNCH(__bf16, 128); else H2O_LAUNCH(__bf16, 64);
+  } else {
+    if (a.d == 128) H2O_LAUNCH(float, 128); else H2O_LAUNCH(float, 64);
+  }
+#undef H2O_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace hubkv

@@ -1,0 +1,96 @@
+// internal.hpp -- shared declarations of the gfx950 KV-retention library.
+//
+// Nothing here is part of the C ABI (include/hubkv.h); these are the launch
+// helpers and device utilities the kernels share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hubkv {
+
+constexpr int kMaxSeqs = 64;
+
+// Per-call sequence table, passed to kernels by value (kernel-argument
+// memory, no device allocation).  `tile_off[b]` is the first tile index of
+// sequence b when every sequence is cut into `tile`-token tiles; tile_off[B]
+// is the total tile count.
+struct SeqTable {
+  int B;
+  int tile;
+  int64_t N[kMaxSeqs];
+  int64_t cu[kMaxSeqs];  // first packed token of each sequence
+  int64_t ko[kMaxSeqs];  // first kept row of each sequence (sum of kept before b)
+  int64_t kept[kMaxSeqs];
+  int32_t tile_off[kMaxSeqs + 1];
+};
+
+// Sequence owning tile `x` (linear scan; B <= 64).
+__device__ __forceinline__ int seq_of_tile(const SeqTable& st, int x) {
+  int b = 0;
+  while (b + 1 < st.B && st.tile_off[b + 1] <= x) ++b;
+  return b;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- score -----------------------------------------------------------------
+// Keys per work-group chunk on the MFMA path and on the fp32 VALU path.
+constexpr int kScoreChunkMfma = 1024;
+constexpr int kScoreChunkF32 = 256;
+
+struct ScoreGeom {
+  int M;       // G * W query rows per KV head
+  int Mpad;    // rows rounded up to 64
+  int chunk;   // keys per work-group
+  int nchunk;  // chunks over all sequences of one (layer, KV head)
+  size_t off_part1, off_rowstat, off_part2, bytes;
+};
+
+ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype);
+
+hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable& st, int L, int Hq,
+                        int Hkv, int W, int d, float scale, int causal, float* s,
+                        double* head_stats, char* ws, const ScoreGeom& geo, hipStream_t stream);
+
+// ---- refine / select ---------------------------------------------------------
+constexpr int kRefineTile = 1024;
+
+struct RefineGeom {
+  int nchunk;
+  size_t off_part, off_stats, off_beta, bytes;
+};
+
+RefineGeom refine_geometry(const SeqTable& st, int L, int Hkv);
+
+hipError_t launch_head_stats(const float* s, const SeqTable& st, int L, int Hkv, double* part,
+                             double* stats, hipStream_t stream);
+
+hipError_t launch_refine(const float* s, const SeqTable& st, int L, int Hkv,
+                         const double* head_stats, const float* beta_in, int pool, float gamma,
+                         float beta_lo, float beta_hi, float r2, float* z, float* beta_out,
+                         float* beta_ws, hipStream_t stream);
+
+hipError_t launch_select(const float* z, const SeqTable& st, int L, int Hkv, int n_sink,
+                         int n_recent, int32_t* idx, hipStream_t stream);
+
+// ---- compaction ------------------------------------------------------------------
+hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, const int32_t* idx,
+                          const SeqTable& st, int L, int Hkv, int d, void* k_out, void* v_out,
+                          hipStream_t stream);
+
+// ---- streaming H2O step ------------------------------------------------------------
+struct H2OArgs {
+  int B, Hq, Hkv, d, C, n_sink, n_recent, include_self;
+  float scale;
+  int64_t t[kMaxSeqs];
+};
+
+hipError_t launch_h2o_step(const void* q, const void* k_new, const void* v_new, int dtype,
+                           void* k_cache, void* v_cache, float* acc, int32_t* pos,
+                           const H2OArgs& a, int32_t* evicted, float* probs, hipStream_t stream);
+
+}  // namespace hubkv
