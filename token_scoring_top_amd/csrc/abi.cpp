@@ -110,7 +110,8 @@ size_t hubkv_score_workspace(int B, const int64_t* seqlens, int L, int Hq, int H
                              int dtype) {
   if (check_dtype_d(dtype, d) != HUBKV_OK) return 0;
   SeqTable st;
-  const int chunk = dtype == HUBKV_BF16 ? kScoreChunkMfma : kScoreChunkF32;
+  if (B < 1 || B > kMaxSeqs || !seqlens) return 0;
+  const int chunk = score_chunk(B, seqlens, dtype);
   if (make_table(st, B, seqlens, chunk) != HUBKV_OK) return 0;
   if (check_score_shape(L, Hq, Hkv, W, st) != HUBKV_OK) return 0;
   return score_geometry(st, L, Hq, Hkv, W, d, dtype).bytes;
@@ -122,7 +123,8 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
   int rc = check_dtype_d(dtype, d);
   if (rc) return rc;
   SeqTable st;
-  const int chunk = dtype == HUBKV_BF16 ? kScoreChunkMfma : kScoreChunkF32;
+  if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
+  const int chunk = score_chunk(B, seqlens, dtype);
   if ((rc = make_table(st, B, seqlens, chunk))) return rc;
   if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
   if (!isfinite(scale)) return HUBKV_EINVAL;

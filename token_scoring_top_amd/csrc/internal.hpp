@@ -38,17 +38,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- score -----------------------------------------------------------------
-// Keys per work-group chunk on the MFMA path and on the fp32 VALU path.
+// Keys per work-group chunk: a multiple of this on the MFMA path (grown for
+// long sequences), fixed on the fp32 VALU path.
 constexpr int kScoreChunkMfma = 1024;
 constexpr int kScoreChunkF32 = 256;
 
 struct ScoreGeom {
   int M;       // G * W query rows per KV head
   int Mpad;    // rows rounded up to 64
-  int chunk;   // keys per work-group
+  int chunk;   // keys per work-group task
   int nchunk;  // chunks over all sequences of one (layer, KV head)
-  size_t off_part1, off_rowstat, off_part2, bytes;
+  size_t off_part1, off_rowstat, off_part2, off_ctl, bytes;
 };
+
+// Chunk size the score path uses for these sequence lengths.
+int score_chunk(int B, const int64_t* seqlens, int dtype);
 
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype);
 

@@ -9,18 +9,19 @@
 // KV head, so their probabilities add up on it).
 //
 // Column sums need each row's softmax normaliser, which depends on every key
-// of the row.  The work is split in two sweeps over the keys so that nothing
-// of size rows x keys is ever stored:
-//   pass 1 (stats)   per work-group chunk of keys and per query row, the
-//                    running maximum m and sum l of exp2(x - m), x the logit
-//                    in log2 units; written as partials;
-//   combine          per row, the partials fold into M = m + log2(l);
-//   pass 2 (probs)   the logits are recomputed and p = exp2(x - M) is summed
-//                    down each key column; per-chunk {sum s, sum s ln s} of
-//                    the finished scores are written for the head weight.
-// bf16 inputs use MFMA (v_mfma_f32_16x16x32_bf16): each wave keeps 64 query
-// rows of Q in registers as A fragments and streams 16-key tiles of K as B
-// fragments straight from global memory.  fp32 inputs use a plain VALU path.
+// of the row, so the keys are swept twice and nothing of size rows x keys is
+// ever stored:
+//   pass 1  per work-group chunk of keys and per query row, the running
+//           maximum m and sum l of exp2(x - m), x the logit in log2 units;
+//   fold    per row, the chunk partials become M = m + log2(l);
+//   pass 2  the logits are recomputed and p = exp2(x - M) is summed down each
+//           key column; per-chunk {sum s, sum s ln s} give the head weight.
+// bf16 inputs use MFMA (v_mfma_f32_32x32x16_bf16): each wave keeps 64 query
+// rows of Q in registers and streams 32-key tiles of K straight from global
+// memory, the next tile in flight while the current one is reduced.  Pass 1
+// puts keys on the MFMA rows (row statistics become lane-local), pass 2 puts
+// queries on the rows (column sums become lane-local).  fp32 inputs use a
+// plain VALU path.
 #include "internal.hpp"
 
 namespace hubkv {
@@ -29,7 +30,6 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMinit = -1.0e30f;   // finite "no key yet" reference
-constexpr float kRescale = 8.0f;     // lazy rescale margin (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -52,19 +52,32 @@ struct ScoreArgs {
 // --------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int score_chunk(int B, const int64_t* seqlens, int dtype) {
+  if (dtype != 1) return kScoreChunkF32;
+  // about 128 chunks for the longest sequence, in multiples of 1024 keys, so
+  // the per-row fold over chunks stays short
+  int64_t mx = 0;
+  for (int b = 0; b < B; ++b) mx = seqlens[b] > mx ? seqlens[b] : mx;
+  int64_t c = (mx + 127) / 128;
+  c = (c + kScoreChunkMfma - 1) / kScoreChunkMfma * kScoreChunkMfma;
+  return (int)(c < kScoreChunkMfma ? kScoreChunkMfma : c);
+}
+
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype) {
   (void)d;
+  (void)dtype;
   ScoreGeom g{};
   g.M = (Hq / Hkv) * W;
   g.Mpad = ((g.M + 63) / 64) * 64;
-  g.chunk = dtype == 1 ? kScoreChunkMfma : kScoreChunkF32;
-  g.nchunk = 0;
-  for (int b = 0; b < st.B; ++b) g.nchunk += (int)((st.N[b] + g.chunk - 1) / g.chunk);
+  g.chunk = st.tile;
+  g.nchunk = st.tile_off[st.B];
   const size_t LH = (size_t)L * Hkv;
+  const size_t U = LH * st.B;
   g.off_part1 = 0;
   g.off_rowstat = align256(LH * g.nchunk * g.Mpad * sizeof(float2));
-  g.off_part2 = g.off_rowstat + align256(LH * st.B * g.Mpad * sizeof(float));
-  g.bytes = g.off_part2 + align256(LH * g.nchunk * 2 * sizeof(double));
+  g.off_part2 = g.off_rowstat + align256(U * g.Mpad * sizeof(float));
+  g.off_ctl = g.off_part2 + align256(LH * g.nchunk * 2 * sizeof(double));
+  g.bytes = g.off_ctl + align256(2 * U * sizeof(int));
   return g;
 }
 
@@ -79,264 +92,347 @@ __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const
 }
 
 // --------------------------------------------------------------------------
-// bf16 MFMA path
+// bf16 MFMA path: two launches over (chunk, layer-head) grids.
+//   pass 1: each work-group reduces its chunk to per-row partials (m, l) and
+//           counts itself in; the work-group that counts last for its unit
+//           (layer-head, sequence) folds all the unit's partials into the row
+//           normalisers M = m + log2(l).
+//   pass 2: each work-group recomputes its chunk's logits, sums p = exp2(x - M)
+//           down every key column, writes s and its chunk's {sum s, sum s ln s};
+//           the last one of a unit adds the unit's chunks up in chunk order.
+// Nobody waits for anybody (the last one to arrive does the fold), so no
+// schedule can deadlock.  The counters live in the workspace and are zeroed
+// by a fill kernel first.  Partials read by the folding work-group go through
+// agent-scope coherent accesses, and a counter is bumped only after the
+// writer's stores completed (s_waitcnt vmcnt(0)), so no cache write-back or
+// invalidation is needed.
 // --------------------------------------------------------------------------
-// Work-group = NRG x NKG waves.  Wave (rg, kg) owns query rows
-// [64 rg, 64 rg + 64) and key tiles kg, kg + NKG, ... of the chunk.
-template <int D, int NRG, int NKG>
-struct MfmaCfg {
-  static constexpr int KS = D / 32;  // k-steps of 32 per MFMA
-  static constexpr int WAVES = NRG * NKG;
-  static constexpr int THREADS = 64 * WAVES;
-};
+constexpr int kSub = 1024;  // keys per column-sum round in pass 2
 
-template <int D, int NRG>
-__device__ __forceinline__ void load_q_frags(bf16x8 (&qa)[4][D / 32], const __bf16* Q,
+__device__ __forceinline__ void st_agent(float2* p, float2 v) {
+  __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_agent(const float2* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load((const unsigned long long*)p,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_agent(double* p, double v) {
+  __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent(const double* p) {
+  return __builtin_bit_cast(double, __hip_atomic_load((const unsigned long long*)p,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ int bump_agent(int* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Query fragments of the wave's 64 rows [64 rg, 64 rg + 64): two 32-row tiles
+// x D/16 k-steps of v_mfma_f32_32x32x16_bf16.  Lane l holds row l % 32 of the
+// tile, head-dimension elements 16 kk + 8 (l / 32) + [0, 8).  The same
+// registers serve as the B operand (pass 1, queries as columns) and as the A
+// operand (pass 2, queries as rows).
+template <int D>
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[2][D / 16], const __bf16* Q,
                                              const ScoreArgs& a, const SeqTable& st, int l, int g,
                                              int b, int rg, int lane) {
-  const int col8 = (lane >> 4) * 8;
+  const int col8 = (lane >> 5) * 8;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = rg * 64 + t * 16 + (lane & 15);
+  for (int qt = 0; qt < 2; ++qt) {
+    const int r = rg * 64 + qt * 32 + (lane & 31);
     if (r < a.M) {
       const __bf16* qr = (const __bf16*)q_row_ptr(Q, 2, a, l, g, st.B, b, r, D);
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) qa[t][kk] = *(const bf16x8*)(qr + kk * 32 + col8);
+      for (int kk = 0; kk < D / 16; ++kk) qf[qt][kk] = *(const bf16x8*)(qr + kk * 16 + col8);
     } else {
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
+      for (int kk = 0; kk < D / 16; ++kk) {
         bf16x8 z;
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
-        qa[t][kk] = z;
+        qf[qt][kk] = z;
       }
     }
   }
 }
 
-// Last visible key (inclusive) of each of the lane's 16 output rows, clamped
-// to the chunk.
-__device__ __forceinline__ void row_limits(int (&lim)[4][4], const ScoreArgs& a, int64_t N,
-                                           int rg, int lane, int64_t chunk_last) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = rg * 64 + t * 16 + (lane >> 4) * 4 + j;
-      int64_t lm;
-      if (r >= a.M) {
-        lm = chunk_last;  // padding row: zero Q, ignored stats, +inf normaliser
-      } else {
-        const int w = r % a.W;
-        lm = a.causal ? (N - a.W + w) : (N - 1);
-        if (lm > chunk_last) lm = chunk_last;
-      }
-      lim[t][j] = (int)lm;
-    }
+// Last visible key (inclusive) of query row r, clamped to `last`.  Padding
+// rows (zero Q, ignored statistics, +inf normaliser) count as fully visible
+// so they do not defeat the full-tile fast path.
+__device__ __forceinline__ int row_limit(const ScoreArgs& a, int N, int r, int last) {
+  if (r >= a.M) return last;
+  const int v = a.causal ? (N - a.W + r % a.W) : (N - 1);
+  return v < last ? v : last;
 }
 
+// Smallest row limit of the wave's 64 rows: tiles ending at or before it need
+// no masking.  Uniform, so callers branch on it with scalar control.
+__device__ __forceinline__ int wave_min_limit(const ScoreArgs& a, int N, int rg, int lane,
+                                              int last) {
+  int v = row_limit(a, N, rg * 64 + lane, last);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Key fragments of a 32-key tile: lane l holds key `key` = key0 + l % 32,
+// elements 16 kk + 8 (l / 32) + [0, 8).  Keys at or past key_end load the
+// last valid key instead (always in bounds, no per-lane branch); callers
+// mask them.
 template <int D>
-__device__ __forceinline__ void load_k_frags(bf16x8 (&kb)[D / 32], const __bf16* Kh, int64_t key,
+__device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[D / 16], const __bf16* Kh, int64_t key,
                                              int64_t key_end, int lane) {
-  const int col8 = (lane >> 4) * 8;
-  if (key < key_end) {
-    const __bf16* kr = Kh + key * D;
+  const int col8 = (lane >> 5) * 8;
+  const int64_t row = key < key_end ? key : key_end - 1;
+  const __bf16* kr = Kh + row * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) kb[kk] = *(const bf16x8*)(kr + kk * 32 + col8);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      bf16x8 z;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
-      kb[kk] = z;
-    }
+  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const bf16x8*)(kr + kk * 16 + col8);
+}
+
+// Output element j of a 32x32 tile sits at row 8 (j / 4) + 4 (lane / 32) +
+// (j % 4) and column lane % 32.
+__device__ __forceinline__ int c_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+// Sweep the 32-key tiles [first, end) with stride STEP, software-pipelined:
+// the next tile's loads are issued before the current tile is reduced, so a
+// wave keeps HBM requests in flight while it computes.  Every path issues the
+// same loads (past-the-end ones are clamped) so the compiler's wait counts
+// stay exact; scheduling barriers keep the loads ahead of the arithmetic.
+// The tile count is uniform, so the loop runs on scalar control.
+template <int D, int STEP, typename F>
+__device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t first, int64_t end,
+                                            int lane, F&& body) {
+  const int ntile = __builtin_amdgcn_readfirstlane(
+      first < end ? (int)((end - first + STEP - 1) / STEP) : 0);
+  if (ntile == 0) return;
+  bf16x8 ka[D / 16], kb[D / 16];
+  load_k_frags<D>(ka, Kh, first + (lane & 31), end, lane);
+  for (int it = 0; it < ntile; it += 2) {
+    const int64_t key0 = first + (int64_t)it * STEP;
+    load_k_frags<D>(kb, Kh, key0 + STEP + (lane & 31), end, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    body(ka, key0);
+    load_k_frags<D>(ka, Kh, key0 + 2 * STEP + (lane & 31), end, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < ntile) body(kb, key0 + STEP);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void mfma_tile(f32x4 (&acc)[4], const bf16x8 (&qa)[4][D / 32],
-                                          const bf16x8 (&kb)[D / 32]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t][kk], kb[kk], c, 0, 0, 0);
-    acc[t] = c;
-  }
-}
-
-template <int D, int NRG, int NKG>
-__global__ __launch_bounds__(64 * NRG * NKG) void score_stats_mfma(const __bf16* __restrict__ Q,
-                                                                    const __bf16* __restrict__ K,
-                                                                    SeqTable st, ScoreArgs a,
-                                                                    float2* __restrict__ part1) {
-  __shared__ float2 red[NKG][64 * NRG];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rg = wave % NRG, kg = wave / NRG;
-  const int lh = blockIdx.y, l = lh / a.Hkv, g = lh % a.Hkv;
-  const int chunk_g = blockIdx.x;
-  const int b = seq_of_tile(st, chunk_g);
-  const int64_t N = st.N[b];
-  const int64_t key_begin = (int64_t)(chunk_g - st.tile_off[b]) * a.chunk;
-  const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
-  const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
-
-  bf16x8 qa[4][D / 32];
-  load_q_frags<D, NRG>(qa, Q, a, st, l, g, b, rg, lane);
-  int lim[4][4];
-  row_limits(lim, a, N, rg, lane, key_end - 1);
-  int minlim = lim[0][0];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) minlim = min(minlim, lim[t][j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) minlim = min(minlim, __shfl_xor(minlim, off));
-
-  float m[4][4], s[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m[t][j] = kMinit;
-      s[t][j] = 0.f;
-    }
-
-  for (int64_t key0 = key_begin + kg * 16; key0 < key_end; key0 += 16 * NKG) {
-    bf16x8 kb[D / 32];
-    const int64_t key = key0 + (lane & 15);
-    load_k_frags<D>(kb, Kh, key, key_end, lane);
-    f32x4 acc[4];
-    mfma_tile<D>(acc, qa, kb);
-    const bool full = (key0 + 15) <= minlim;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (full || key <= lim[t][j]) {
-          const float x = acc[t][j] * a.c2;
-          float dl = x - m[t][j];
-          if (dl > kRescale) {  // new reference well above the old one
-            s[t][j] *= fast_exp2(m[t][j] - x);
-            m[t][j] = x;
-            dl = 0.f;
-          }
-          s[t][j] += fast_exp2(dl);
-        }
-      }
-  }
-  // fold the 16 key columns of each row (lanes differing in bits 0..3)
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float m2 = __shfl_xor(m[t][j], off);
-        const float s2 = __shfl_xor(s[t][j], off);
-        merge_ml(m[t][j], s[t][j], m2, s2);
-      }
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rl = rg * 64 + t * 16 + (lane >> 4) * 4 + j;
-        red[kg][rl] = make_float2(m[t][j], s[t][j]);
-      }
-  }
-  __syncthreads();
-  for (int rl = threadIdx.x; rl < 64 * NRG; rl += 64 * NRG * NKG) {
-    float mm = red[0][rl].x, ss = red[0][rl].y;
-#pragma unroll
-    for (int q = 1; q < NKG; ++q) merge_ml(mm, ss, red[q][rl].x, red[q][rl].y);
-    if (rl < a.Mpad)
-      part1[((int64_t)lh * a.nchunk + chunk_g) * a.Mpad + rl] = make_float2(mm, ss);
-  }
-}
-
-template <int D, int NRG, int NKG>
-__global__ __launch_bounds__(64 * NRG * NKG) void score_probs_mfma(
+template <int D, int NRG, int NKG, int PHASE>
+__global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, SeqTable st, ScoreArgs a,
-    const float* __restrict__ rowstat, float* __restrict__ s_out, double2* __restrict__ part2) {
-  constexpr int CK = kScoreChunkMfma;
-  __shared__ float cs[NRG][CK];
-  __shared__ double2 hred[64 * NRG * NKG / 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int* __restrict__ ctl, float2* __restrict__ part1, float* __restrict__ rowstat,
+    double2* __restrict__ part2, float* __restrict__ s_out, double* __restrict__ stats) {
+  constexpr int TH = 64 * NRG * NKG;
+  constexpr int WAVES = NRG * NKG;
+  constexpr int STEP = 32 * NKG;
+  constexpr int KS = D / 16;
+  const int U = a.L * a.Hkv * st.B;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int rg = wave % NRG, kg = wave / NRG;
-  const int lh = blockIdx.y, l = lh / a.Hkv, g = lh % a.Hkv;
-  const int chunk_g = blockIdx.x;
+  const int lh = blockIdx.y, chunk_g = blockIdx.x;
   const int b = seq_of_tile(st, chunk_g);
-  const int64_t N = st.N[b];
-  const int64_t key_begin = (int64_t)(chunk_g - st.tile_off[b]) * a.chunk;
+  const int c = chunk_g - st.tile_off[b];
+  const int u = lh * st.B + b;
+  const int l = lh / a.Hkv, g = lh - l * a.Hkv;
+  const int nch = st.tile_off[b + 1] - st.tile_off[b];
+  const int N = (int)st.N[b];
+  const int64_t key_begin = (int64_t)c * a.chunk;
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
   const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
 
-  bf16x8 qa[4][D / 32];
-  load_q_frags<D, NRG>(qa, Q, a, st, l, g, b, rg, lane);
-  int lim[4][4];
-  row_limits(lim, a, N, rg, lane, key_end - 1);
-  int minlim = lim[0][0];
-  float Mr[4][4];
-  const float* rs = rowstat + ((int64_t)lh * st.B + b) * a.Mpad;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      minlim = min(minlim, lim[t][j]);
-      Mr[t][j] = rs[rg * 64 + t * 16 + (lane >> 4) * 4 + j];
-    }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) minlim = min(minlim, __shfl_xor(minlim, off));
+  bf16x8 qf[2][KS];
+  load_q_frags<D>(qf, Q, a, st, l, g, b, rg, lane);
 
-  for (int64_t key0 = key_begin + kg * 16; key0 < key_end; key0 += 16 * NKG) {
-    bf16x8 kb[D / 32];
-    const int64_t key = key0 + (lane & 15);
-    load_k_frags<D>(kb, Kh, key, key_end, lane);
-    f32x4 acc[4];
-    mfma_tile<D>(acc, qa, kb);
-    const bool full = (key0 + 15) <= minlim;
-    float c = 0.f;
+  if constexpr (PHASE == 1) {
+    // ---- pass 1: keys as MFMA rows, queries as columns: lane l owns query
+    // row 64 rg + 32 qt + l % 32 and 16 of the tile's keys, so the running
+    // row maximum and sum are lane-local.
+    __shared__ float2 red[NKG][64 * NRG];
+    __shared__ int sh_last;
+    int* arrive = ctl;
+    const int last = (int)key_end - 1;
+    const int minlim = wave_min_limit(a, N, rg, lane, last);
+    int lim[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int qt = 0; qt < 2; ++qt) lim[qt] = row_limit(a, N, rg * 64 + qt * 32 + (lane & 31), last);
+    float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
+    sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane,
+                         [&](const bf16x8 (&kf)[KS], int64_t key0) {
+      const bool full = (int)key0 + 31 <= minlim;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(acc[t][j] * a.c2 - Mr[t][j]);
-        c += (full || key <= lim[t][j]) ? p : 0.f;
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[qt][kk], acc, 0, 0, 0);
+        if (!full) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if ((int)key0 + c_row(j, lane) > lim[qt]) acc[j] = -INFINITY;
+        }
+        float tmax = acc[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, acc[j]);
+        const float mn = fmaxf(m[qt], tmax * a.c2);
+        const float mref = fmaxf(mn, -1.0e30f);  // all keys masked so far: stay at zero
+        float add = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) add += fast_exp2(fmaf(acc[j], a.c2, -mref));
+        s[qt] = fmaf(s[qt], fast_exp2(m[qt] - mref), add);
+        m[qt] = mn;
       }
-    c += __shfl_xor(c, 16);
-    c += __shfl_xor(c, 32);
-    if (lane < 16) cs[rg][key0 - key_begin + lane] = c;
-  }
-  __syncthreads();
-  // finish the column sums, write s, and accumulate the head statistics
-  double hs = 0.0, ha = 0.0;
-  float* so = s_out + (int64_t)lh * a.T + st.cu[b];
-  for (int i = threadIdx.x; i < key_end - key_begin; i += 64 * NRG * NKG) {
-    float v = cs[0][i];
+    });
+    // lanes l and l + 32 hold the same rows over different keys
 #pragma unroll
-    for (int q = 1; q < NRG; ++q) v += cs[q][i];
-    so[key_begin + i] = v;
-    hs += (double)v;
-    if (v > 0.f) ha += (double)v * (double)(__builtin_amdgcn_logf(v) * kLn2);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    hs += __shfl_xor(hs, off);
-    ha += __shfl_xor(ha, off);
-  }
-  if (lane == 0) hred[wave] = make_double2(hs, ha);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double S = 0.0, A = 0.0;
-    for (int w = 0; w < NRG * NKG; ++w) {
-      S += hred[w].x;
-      A += hred[w].y;
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m2 = __shfl_xor(m[qt], 32), s2 = __shfl_xor(s[qt], 32);
+      const float mn = fmaxf(m[qt], m2);
+      const float mref = fmaxf(mn, -1.0e30f);
+      s[qt] = s[qt] * fast_exp2(m[qt] - mref) + s2 * fast_exp2(m2 - mref);
+      m[qt] = mn;
+      if (lane < 32) red[kg][rg * 64 + qt * 32 + lane] = make_float2(fmaxf(m[qt], kMinit), s[qt]);
     }
-    part2[(int64_t)lh * a.nchunk + chunk_g] = make_double2(S, A);
+    __syncthreads();
+    // wave 0 publishes the chunk's partials, then counts the chunk in
+    if (wave == 0) {
+      for (int rl = lane; rl < a.Mpad; rl += 64) {
+        float mm = red[0][rl].x, ss = red[0][rl].y;
+#pragma unroll
+        for (int q = 1; q < NKG; ++q) merge_ml(mm, ss, red[q][rl].x, red[q][rl].y);
+        st_agent(&part1[((int64_t)lh * a.nchunk + chunk_g) * a.Mpad + rl], make_float2(mm, ss));
+      }
+      wait_stores();
+      if (lane == 0) sh_last = (bump_agent(&arrive[u]) == nch - 1);
+    }
+    __syncthreads();
+    if (sh_last) {
+      // the unit's last chunk: fold every chunk's partials into M = m + log2(l)
+      const float2* pp = part1 + ((int64_t)lh * a.nchunk + st.tile_off[b]) * a.Mpad;
+      for (int r = tid; r < a.Mpad; r += TH) {
+        float mm = kMinit, ss = 0.f;
+        for (int cc = 0; cc < nch; cc += 8) {
+          float2 pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pv[e] = cc + e < nch ? ld_agent(&pp[(int64_t)(cc + e) * a.Mpad + r])
+                                 : make_float2(kMinit, 0.f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (pv[e].y > 0.f) merge_ml(mm, ss, pv[e].x, pv[e].y);
+        }
+        rowstat[(int64_t)u * a.Mpad + r] =
+            (r < a.M && ss > 0.f) ? mm + __builtin_amdgcn_logf(ss) : INFINITY;
+      }
+    }
+  } else {
+    // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
+    // key0 + l % 32 and 16 rows of each query tile, so a column sum is a
+    // lane-local sum plus one exchange between the two half-waves.
+    __shared__ float cs[NRG][kSub];
+    __shared__ double2 hred[WAVES];
+    // row normalisers in LDS: a lane's 16 rows of a query tile are 4 runs of
+    // 4 consecutive rows, the same for every lane of a half-wave, so they are
+    // read as broadcast float4s instead of being held in 32 registers
+    __shared__ __attribute__((aligned(16))) float mrow[64 * NRG];
+    int* done2 = ctl + U;
+    const float* rs = rowstat + (int64_t)u * a.Mpad;
+    for (int r = tid; r < a.Mpad; r += TH) mrow[r] = rs[r];
+    __syncthreads();
+    double hs = 0.0, ha = 0.0;
+    float* so = s_out + (int64_t)lh * a.T + st.cu[b];
+    for (int64_t sub0 = key_begin; sub0 < key_end; sub0 += kSub) {
+      const int64_t sub1 = sub0 + kSub < key_end ? sub0 + kSub : key_end;
+      const int last = (int)sub1 - 1;
+      const int minlim = wave_min_limit(a, N, rg, lane, last);
+      sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane,
+                           [&](const bf16x8 (&kf)[KS], int64_t key0) {
+        const int key = (int)key0 + (lane & 31);
+        const bool full = (int)key0 + 31 <= minlim;
+        float cv = 0.f;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][kk], kf[kk], acc, 0, 0, 0);
+          float Mr[16];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 v = *(const f32x4*)&mrow[rg * 64 + qt * 32 + 8 * jj + 4 * (lane >> 5)];
+            Mr[4 * jj] = v[0];
+            Mr[4 * jj + 1] = v[1];
+            Mr[4 * jj + 2] = v[2];
+            Mr[4 * jj + 3] = v[3];
+          }
+          if (full) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cv += fast_exp2(fmaf(acc[j], a.c2, -Mr[j]));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float p = fast_exp2(fmaf(acc[j], a.c2, -Mr[j]));
+              const int r = rg * 64 + qt * 32 + c_row(j, lane);
+              cv += key <= row_limit(a, N, r, last) ? p : 0.f;
+            }
+          }
+        }
+        cv += __shfl_xor(cv, 32);
+        if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
+      });
+      __syncthreads();
+      for (int i = tid; i < sub1 - sub0; i += TH) {
+        float v = cs[0][i];
+#pragma unroll
+        for (int q = 1; q < NRG; ++q) v += cs[q][i];
+        so[sub0 + i] = v;
+        hs += (double)v;
+        if (v > 0.f) ha += (double)v * (double)(__builtin_amdgcn_logf(v) * kLn2);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      hs += __shfl_xor(hs, off);
+      ha += __shfl_xor(ha, off);
+    }
+    if (lane == 0) hred[wave] = make_double2(hs, ha);
+    __syncthreads();
+    if (tid == 0) {
+      double S = 0.0, A = 0.0;
+      for (int w = 0; w < WAVES; ++w) {
+        S += hred[w].x;
+        A += hred[w].y;
+      }
+      double* p2w = (double*)&part2[(int64_t)lh * a.nchunk + chunk_g];
+      st_agent(p2w, S);
+      st_agent(p2w + 1, A);
+      wait_stores();
+      if (bump_agent(&done2[u]) == nch - 1 && stats) {
+        // the unit's last chunk: head statistics, chunks added in order
+        double S2 = 0.0, A2 = 0.0;
+        const double* p2 = (const double*)(part2 + (int64_t)lh * a.nchunk + st.tile_off[b]);
+        for (int cc = 0; cc < nch; ++cc) {
+          S2 += ld_agent(p2 + 2 * cc);
+          A2 += ld_agent(p2 + 2 * cc + 1);
+        }
+        const int64_t su = (((int64_t)l * st.B + b) * a.Hkv + g) * 2;
+        stats[su] = S2;
+        stats[su + 1] = A2;
+      }
+    }
   }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_i32(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // --------------------------------------------------------------------------
@@ -511,24 +607,6 @@ __global__ __launch_bounds__(64) void stats_final(SeqTable st, int L, int Hkv, i
   stats[(int64_t)u * 2 + 1] = A;
 }
 
-template <int D, int NRG, int NKG>
-hipError_t run_mfma(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
-                    float2* part1, float* rowstat, float* s, double2* part2, hipStream_t stream) {
-  constexpr int TH = 64 * NRG * NKG;
-  const dim3 grid(a.nchunk, a.L * a.Hkv);
-  hipLaunchKernelGGL((score_stats_mfma<D, NRG, NKG>), grid, dim3(TH), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, st, a, part1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_combine, dim3((a.Mpad + 255) / 256, st.B, a.L * a.Hkv), dim3(256), 0,
-                     stream, st, a, (const float2*)part1, rowstat);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((score_probs_mfma<D, NRG, NKG>), grid, dim3(TH), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, st, a, (const float*)rowstat, s, part2);
-  return hipGetLastError();
-}
-
 template <int D>
 hipError_t run_f32(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
                    float2* part1, float* rowstat, float* s, double2* part2, hipStream_t stream) {
@@ -546,20 +624,41 @@ hipError_t run_f32(const void* q, const void* k, const SeqTable& st, const Score
   return hipGetLastError();
 }
 
+template <int D, int NRG, int NKG>
+hipError_t run_mfma(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
+                    char* ws, const ScoreGeom& geo, float* s, double* stats,
+                    hipStream_t stream) {
+  const int U = a.L * a.Hkv * st.B;
+  int* ctl = (int*)(ws + geo.off_ctl);
+  hipLaunchKernelGGL(fill_zero_i32, dim3((2 * U + 255) / 256), dim3(256), 0, stream, ctl, 2 * U);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.nchunk, a.L * a.Hkv), block(64 * NRG * NKG);
+  float2* part1 = (float2*)(ws + geo.off_part1);
+  float* rowstat = (float*)(ws + geo.off_rowstat);
+  double2* part2 = (double2*)(ws + geo.off_part2);
+  hipLaunchKernelGGL((score_pass_mfma<D, NRG, NKG, 1>), grid, block, 0, stream, (const __bf16*)q,
+                     (const __bf16*)k, st, a, ctl, part1, rowstat, part2, s, stats);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((score_pass_mfma<D, NRG, NKG, 2>), grid, block, 0, stream, (const __bf16*)q,
+                     (const __bf16*)k, st, a, ctl, part1, rowstat, part2, s, stats);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dispatch_mfma(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
-                         float2* part1, float* rowstat, float* s, double2* part2,
+                         char* ws, const ScoreGeom& geo, float* s, double* stats,
                          hipStream_t stream) {
-  const int nrg = a.Mpad / 64;
-  switch (nrg) {
-    case 1: return run_mfma<D, 1, 4>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 2: return run_mfma<D, 2, 2>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 3: return run_mfma<D, 3, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 4: return run_mfma<D, 4, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 5: return run_mfma<D, 5, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 6: return run_mfma<D, 6, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 7: return run_mfma<D, 7, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
-    case 8: return run_mfma<D, 8, 1>(q, k, st, a, part1, rowstat, s, part2, stream);
+  switch (a.Mpad / 64) {
+    case 1: return run_mfma<D, 1, 4>(q, k, st, a, ws, geo, s, stats, stream);
+    case 2: return run_mfma<D, 2, 2>(q, k, st, a, ws, geo, s, stats, stream);
+    case 3: return run_mfma<D, 3, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 4: return run_mfma<D, 4, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 5: return run_mfma<D, 5, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 6: return run_mfma<D, 6, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 7: return run_mfma<D, 7, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 8: return run_mfma<D, 8, 1>(q, k, st, a, ws, geo, s, stats, stream);
     default: return hipErrorInvalidValue;  // G*W > 512 is rejected before launch
   }
 }
@@ -583,17 +682,14 @@ hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable&
   a.T = 0;
   for (int b = 0; b < st.B; ++b) a.T += st.N[b];
   a.c2 = (float)((double)scale * 1.4426950408889634);
+  if (dtype == 1)
+    return d == 128 ? dispatch_mfma<128>(q, k, st, a, ws, geo, s, head_stats, stream)
+                    : dispatch_mfma<64>(q, k, st, a, ws, geo, s, head_stats, stream);
   float2* part1 = (float2*)(ws + geo.off_part1);
   float* rowstat = (float*)(ws + geo.off_rowstat);
   double2* part2 = (double2*)(ws + geo.off_part2);
-  hipError_t e;
-  if (dtype == 1) {
-    e = d == 128 ? dispatch_mfma<128>(q, k, st, a, part1, rowstat, s, part2, stream)
-                 : dispatch_mfma<64>(q, k, st, a, part1, rowstat, s, part2, stream);
-  } else {
-    e = d == 128 ? run_f32<128>(q, k, st, a, part1, rowstat, s, part2, stream)
-                 : run_f32<64>(q, k, st, a, part1, rowstat, s, part2, stream);
-  }
+  hipError_t e = d == 128 ? run_f32<128>(q, k, st, a, part1, rowstat, s, part2, stream)
+                          : run_f32<64>(q, k, st, a, part1, rowstat, s, part2, stream);
   if (e != hipSuccess || !head_stats) return e;
   const int units = L * st.B * Hkv;
   hipLaunchKernelGGL(stats_final, dim3((units + 63) / 64), dim3(64), 0, stream, st, L, Hkv,
