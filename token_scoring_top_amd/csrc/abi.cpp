@@ -178,7 +178,7 @@ int hubkv_refine(const float* s, int B, const int64_t* seqlens, int L, int Hkv,
   }
   const float r2 = r * r;  // fp32 product, as the gate formula is evaluated in fp32
   return hip_status(launch_refine(s, st, L, Hkv, stats, beta_in, pool, gamma, beta_lo, beta_hi, r2,
-                                  z, beta_out, (float*)(ws + geo.off_beta), strm));
+                                  z, beta_out, strm));
 }
 
 int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,

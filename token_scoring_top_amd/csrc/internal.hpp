@@ -65,7 +65,7 @@ constexpr int kRefineTile = 1024;
 
 struct RefineGeom {
   int nchunk;
-  size_t off_part, off_stats, off_beta, bytes;
+  size_t off_part, off_stats, bytes;
 };
 
 RefineGeom refine_geometry(const SeqTable& st, int L, int Hkv);
@@ -76,7 +76,7 @@ hipError_t launch_head_stats(const float* s, const SeqTable& st, int L, int Hkv,
 hipError_t launch_refine(const float* s, const SeqTable& st, int L, int Hkv,
                          const double* head_stats, const float* beta_in, int pool, float gamma,
                          float beta_lo, float beta_hi, float r2, float* z, float* beta_out,
-                         float* beta_ws, hipStream_t stream);
+                         hipStream_t stream);
 
 hipError_t launch_select(const float* z, const SeqTable& st, int L, int Hkv, int n_sink,
                          int n_recent, int32_t* idx, hipStream_t stream);

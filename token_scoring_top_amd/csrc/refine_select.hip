@@ -14,9 +14,8 @@
 // the lower position, written ascending.
 //
 // Selection is an exact radix select on order-preserving 32-bit keys of z
-// (three histogram passes of 11, 11 and 10 bits in LDS), followed by one
-// ordered emission pass in which each wave walks a contiguous segment and
-// uses ballots for the in-order ranks of ties and of kept positions.  The
+// (histogram passes in LDS, the first one over the keys' own range), followed
+// by one ordered emission pass that ranks kept positions with ballots.  The
 // result is deterministic and independent of thread timing.
 #include "internal.hpp"
 
@@ -31,8 +30,7 @@ RefineGeom refine_geometry(const SeqTable& st, int L, int Hkv) {
   const size_t LH = (size_t)L * Hkv;
   g.off_part = 0;
   g.off_stats = align256r(LH * g.nchunk * 2 * sizeof(double));
-  g.off_beta = g.off_stats + align256r((size_t)L * st.B * Hkv * 2 * sizeof(double));
-  g.bytes = g.off_beta + align256r((size_t)L * st.B * Hkv * sizeof(float));
+  g.bytes = g.off_stats + align256r((size_t)L * st.B * Hkv * 2 * sizeof(double));
   return g;
 }
 
@@ -95,40 +93,35 @@ __global__ __launch_bounds__(64) void head_stats_final(SeqTable st, int L, int H
   stats[(int64_t)u * 2 + 1] = A;
 }
 
-// Head weight of every (layer, sequence, KV head): one work-group per
-// (layer, sequence), one thread per KV head, the mean over heads by shuffles.
-constexpr int kMaxHkvBeta = 1024;
-
-__global__ __launch_bounds__(kMaxHkvBeta) void beta_kernel(SeqTable st, int Hkv,
-                                                           const double* __restrict__ stats,
-                                                           float lo, float hi,
-                                                           float* __restrict__ beta) {
-  __shared__ double part[kMaxHkvBeta / 64];
-  const int lb = blockIdx.x;  // l * B + b
-  const int b = lb % st.B;
-  const int g = threadIdx.x;
+// Head weight of KV head g of (layer, sequence) lb, computed by wave 0 of a
+// work-group: sel = 1 - (ln S - A / S) / ln N per head from {S, A} =
+// {sum s, sum s ln s}, beta = clip(sel_g / mean_heads sel, lo, hi), 1 when the
+// mean is not positive.  Every lane ends with beta.
+__device__ float head_beta(const SeqTable& st, int lb, int b, int g, int Hkv,
+                           const double* __restrict__ stats, float lo, float hi) {
+  const int lane = threadIdx.x & 63;
   const double lnN = log((double)st.N[b]);
-  double v = 0.0;
-  if (g < Hkv) {
-    const double S = stats[((int64_t)lb * Hkv + g) * 2], A = stats[((int64_t)lb * Hkv + g) * 2 + 1];
+  double sum = 0.0, mine = 0.0;
+  for (int h = lane; h < Hkv; h += 64) {
+    const double S = stats[((int64_t)lb * Hkv + h) * 2], A = stats[((int64_t)lb * Hkv + h) * 2 + 1];
+    double v = 0.0;
     if (st.N[b] > 1 && S > 0.0) v = 1.0 - (log(S) - A / S) / lnN;
+    sum += v;
+    if (h == g) mine = v;
   }
-  double sum = v;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
-  __syncthreads();
-  if (g >= Hkv) return;
-  double mean = 0.0;
-  for (int w = 0; w < (int)((blockDim.x + 63) / 64); ++w) mean += part[w];
-  mean /= (double)Hkv;
+  for (int off = 32; off >= 1; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    mine += __shfl_xor(mine, off);  // one lane holds it, the others add 0
+  }
+  const double mean = sum / (double)Hkv;
   double bt = 1.0;
   if (mean > 0.0 && isfinite(mean)) {
-    bt = v / mean;
+    bt = mine / mean;
     if (bt < (double)lo) bt = (double)lo;
     if (bt > (double)hi) bt = (double)hi;
   }
-  beta[(int64_t)lb * Hkv + g] = (float)bt;
+  return (float)bt;
 }
 
 // ---------------------------------------------------------------------------
@@ -136,6 +129,7 @@ __global__ __launch_bounds__(kMaxHkvBeta) void beta_kernel(SeqTable st, int Hkv,
 // sequence per work-group, staged with its halo in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kMaxHalf = 31;
+constexpr int kRefineThreads = 256;
 
 // SMD discount and ratio gate as this exact fp32 op sequence (no contraction):
 // q = hub ? s : fl(gamma s); z = fma(r2, fl(fl(beta q) - s), s).
@@ -147,257 +141,340 @@ __device__ __forceinline__ float smd_gate(float si, bool hub, float gamma, float
   return __builtin_fmaf(r2, d, si);
 }
 
-__global__ __launch_bounds__(256) void refine_kernel(const float* __restrict__ s, SeqTable st,
-                                                     int64_t T, int Hkv, int half, float gamma,
-                                                     float r2, const float* __restrict__ beta,
-                                                     float* __restrict__ z,
-                                                     float* __restrict__ beta_out) {
+__global__ __launch_bounds__(kRefineThreads) void refine_kernel(
+    const float* __restrict__ s, SeqTable st, int64_t T, int Hkv, int half, float gamma, float r2,
+    const float* __restrict__ beta_in, const double* __restrict__ stats, float lo, float hi,
+    float* __restrict__ z, float* __restrict__ beta_out) {
   __shared__ float tile[kRefineTile + 2 * kMaxHalf];
+  __shared__ float sh_beta;
   const int lh = blockIdx.y, c = blockIdx.x;
   const int l = lh / Hkv, g = lh % Hkv;
   const int b = seq_of_tile(st, c);
-  const int64_t N = st.N[b];
-  const int64_t i0 = (int64_t)(c - st.tile_off[b]) * kRefineTile;
+  const int N = (int)st.N[b];
+  const int i0 = (c - st.tile_off[b]) * kRefineTile;
   const float* sb = s + (int64_t)lh * T + st.cu[b];
   float* zb = z + (int64_t)lh * T + st.cu[b];
-  const int u = (l * st.B + b) * Hkv + g;
-  const float bt = beta[u];
-  if (beta_out && i0 == 0 && threadIdx.x == 0) beta_out[u] = bt;
-  // tile[j] holds s[i0 - half + j]
-  for (int j = threadIdx.x; j < kRefineTile + 2 * half; j += 256) {
-    const int64_t i = i0 - half + j;
+  const int lb = l * st.B + b;
+  const int u = lb * Hkv + g;
+  // tile[j] holds s[i0 - half + j] (0 outside the sequence, never read)
+  for (int j = threadIdx.x; j < kRefineTile + 2 * half; j += kRefineThreads) {
+    const int i = i0 - half + j;
     tile[j] = (i >= 0 && i < N) ? sb[i] : 0.f;
   }
-  __syncthreads();
-  for (int j = threadIdx.x; j < kRefineTile; j += 256) {
-    const int64_t i = i0 + j;
-    if (i >= N) break;
-    const int64_t lo = i - half < 0 ? 0 : i - half;
-    const int64_t hi = i + half > N - 1 ? N - 1 : i + half;
-    float mx = tile[lo - i0 + half];
-    for (int64_t k = lo + 1; k <= hi; ++k) {
-      const float v = tile[k - i0 + half];
-      mx = v > mx ? v : mx;
+  if (threadIdx.x < 64) {
+    const float bt = beta_in ? beta_in[u] : head_beta(st, lb, b, g, Hkv, stats, lo, hi);
+    if (threadIdx.x == 0) {
+      sh_beta = bt;
+      if (beta_out && i0 == 0) beta_out[u] = bt;
     }
+  }
+  __syncthreads();
+  const float bt = sh_beta;
+  // window max scanned from its lowest in-sequence position upwards with a
+  // strict compare, so that a NaN first entry stays the max as in a plain scan
+  for (int j = threadIdx.x; j < kRefineTile; j += kRefineThreads) {
+    const int i = i0 + j;
+    if (i >= N) break;
     const float si = tile[j + half];
+    float mx;
+    if (half == 2 && i >= 2 && i + 2 < N) {
+      mx = tile[j];
+      mx = tile[j + 1] > mx ? tile[j + 1] : mx;
+      mx = si > mx ? si : mx;
+      mx = tile[j + 3] > mx ? tile[j + 3] : mx;
+      mx = tile[j + 4] > mx ? tile[j + 4] : mx;
+    } else {
+      const int wlo = i - half < 0 ? 0 : i - half;
+      const int whi = i + half > N - 1 ? N - 1 : i + half;
+      mx = tile[wlo - i0 + half];
+      for (int k = wlo + 1; k <= whi; ++k) {
+        const float v = tile[k - i0 + half];
+        mx = v > mx ? v : mx;
+      }
+    }
     zb[i] = smd_gate(si, si == mx, gamma, bt, r2);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Protected Top-K by radix select.
+// Protected Top-K by radix select, one work-group per (layer, KV head,
+// sequence).
+//
+// Layout: the sequence is cut into rounds of kSelRound positions; inside a
+// round wave w owns kSelKpt sub-blocks of 64 consecutive positions and lane l
+// holds position (w * kSelKpt + j) * 64 + l of sub-block j, so every load is a
+// fully coalesced 256-byte row and position order inside a sub-block is lane
+// order (ballots give in-order ranks).  A sequence of one round keeps its
+// keys in registers through every pass; longer ones reload each round from L2.
+//
+// Keys: order-preserving 32-bit images of z (NaN lowest, -0 == +0), at most
+// 0xff800000 (+inf).  Protected positions get kProt, above every real key, and
+// positions past the end get kPad; neither is ever a candidate.  Once the
+// candidates' range [kmin, kmax] is known, candidate keys are rebased to
+// v = key - kmin in place.  Pass 1 bins v >> sh with the smallest shift that
+// fits the range into 2047 bins (about 2047 occupied bins, few LDS-atomic
+// collisions), protected and padding keys counted in bin 2047; further passes
+// resolve the remaining low bits 11 at a time inside the chosen bin.  The
+// result is (thr, rem): every key above thr is kept, plus the first rem keys
+// equal to thr in position order.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelKpt = 32;
+constexpr int kSelRound = kSelThreads * kSelKpt;
+constexpr uint32_t kProt = 0xffffffffu;
+constexpr uint32_t kPad = 0xfffffffeu;
 
 __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
-  if (v != v) return 0u;             // NaN ranks below everything
-  if (u == 0x80000000u) u = 0u;      // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = u == 0x80000000u ? 0u : u;                            // -0 == +0
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return v != v ? 0u : k;                                   // NaN ranks below everything
 }
 
 __device__ __forceinline__ unsigned long long lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive scan over the kSelWaves wave totals held in shared memory.
-__device__ __forceinline__ void wave_totals_scan(uint32_t* v) {
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t x = v[w];
-      v[w] = run;
-      run += x;
-    }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off);
+    v = o < v ? o : v;
   }
+  return v;
 }
 
-// Keys of candidate positions [a, c) of one (layer, head, sequence): staged in
-// LDS when they fit, else read from global memory (z stays in L2).
-constexpr int kSelLdsKeys = 36864;  // 144 KiB
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
 
-template <bool kLds>
-struct KeySource {
+struct SelView {
   const float* zb;
-  const uint32_t* lds;
-  int64_t a;
-  __device__ __forceinline__ uint32_t operator()(int64_t i) const {
-    if constexpr (kLds) return lds[i - a];
-    else return order_key(zb[i]);
+  int N, a, c, wave, lane;
+  __device__ __forceinline__ int base(int r) const {
+    return r * kSelRound + wave * (64 * kSelKpt) + lane;
+  }
+  // keys of round r; a position past N reads a clamped address and gets kPad
+  __device__ __forceinline__ void load(int r, uint32_t (&key)[kSelKpt]) const {
+    const int p0 = base(r);
+    float v[kSelKpt];
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      const int p = p0 + 64 * j;
+      v[j] = zb[p < N ? p : N - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      const int p = p0 + 64 * j;
+      const uint32_t k = order_key(v[j]);
+      const uint32_t kp = (p < a || p >= c) ? kProt : k;
+      key[j] = p >= N ? kPad : kp;
+    }
+  }
+  // rebase candidate keys to key - kmin (special keys unchanged)
+  __device__ __forceinline__ void rebase(uint32_t (&key)[kSelKpt], uint32_t kmn) const {
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
   }
 };
 
-template <bool kLds>
-__device__ void select_body(const float* __restrict__ zb, int32_t* __restrict__ out, int64_t N,
-                            int64_t kept, int n_sink, int n_recent, uint32_t* keys,
-                            uint32_t* hist, uint32_t* wt_def, uint32_t* wt_tie, uint32_t* wt_keep,
-                            uint32_t* sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // protected: [0, a) and [c, N)
-  const int64_t a = n_sink < N ? n_sink : N;
-  int64_t c = N - n_recent > 0 ? N - n_recent : 0;
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ z,
+                                                             SeqTable st, int64_t T, int64_t Ktot,
+                                                             int n_sink, int n_recent,
+                                                             int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wa[kSelWaves], wb[kSelWaves];
+  __shared__ uint32_t bc[2];
+  const int lh = blockIdx.y, b = blockIdx.x;
+  const int N = (int)st.N[b];
+  const int kept = (int)st.kept[b];
+  if (N <= 0 || kept <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int a = n_sink < N ? n_sink : N;
+  int c = N - n_recent > 0 ? N - n_recent : 0;
   if (c < a) c = a;
-  const int64_t ncand = c - a;
-  const int64_t want = kept - (a + (N - c));
-  const int mode = (want <= 0) ? 0 : (want >= ncand ? 1 : 2);
-  if (kLds && mode == 2) {
-    // stage the candidates' order keys, four loads in flight per thread
-    for (int64_t i0 = tid; i0 < ncand; i0 += 4 * kSelThreads) {
-      float v[4];
+  const uint32_t nprot = (uint32_t)(a + (N - c));
+  const SelView sv{z + (int64_t)lh * T + st.cu[b], N, a, c, wave, lane};
+  int32_t* out = idx + (int64_t)lh * Ktot + st.ko[b];
+  const int nr = (N + kSelRound - 1) / kSelRound;
+  const uint32_t npad = (uint32_t)(nr * kSelRound - N);
+
+  uint32_t key[kSelKpt];
+  sv.load(0, key);
+
+  // keep rule: key > thr (kPad excluded), or key == thr among the first rem
+  // such keys in position order; keys are rebased when a select ran
+  uint32_t thr, rem, kmn = 0u;
+  bool rebased = false;
+  if ((uint32_t)kept >= (uint32_t)N) {
+    thr = 0u;
+    rem = (uint32_t)N;
+  } else if ((uint32_t)kept <= nprot) {
+    thr = kProt;
+    rem = (uint32_t)kept;
+  } else {
+    // range of the candidate keys
+    uint32_t mn = kPad, mx = 0u;
+    for (int r = 0; r < nr; ++r) {
+      if (nr > 1) sv.load(r, key);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u * kSelThreads;
-        v[u] = i < ncand ? zb[a + i] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u * kSelThreads;
-        if (i < ncand) keys[i] = order_key(v[u]);
+      for (int j = 0; j < kSelKpt; ++j) {
+        const uint32_t k = key[j];
+        mn = k < mn ? k : mn;                    // specials are >= kPad
+        mx = (k < kPad && k > mx) ? k : mx;
       }
     }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+      wa[wave] = mn;
+      wb[wave] = mx;
+    }
     __syncthreads();
-  }
-  const KeySource<kLds> key_at{zb, keys, a};
+    mn = kPad;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      mn = wa[w] < mn ? wa[w] : mn;
+      mx = wb[w] > mx ? wb[w] : mx;
+    }
+    kmn = mn;
+    rebased = true;
+    const uint32_t range = mx - mn;  // <= 0xff800000, so sh <= 21
+    int sh = 0;
+    while ((range >> sh) > 2046u) ++sh;
+    if (nr == 1) sv.rebase(key, kmn);
 
-  uint32_t thr = 0, rem = 0;
-  if (mode == 2) {
-    uint32_t prefix = 0, pmask = 0;
-    uint32_t need = (uint32_t)want;
-    const int shifts[3] = {21, 10, 0};
-    const int bits[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int nb = 1 << bits[pass];
-      const int shf = shifts[pass];
-      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+    // counted from the top: protected keys and padding sit in bin 2047
+    uint32_t need = (uint32_t)kept + npad;
+    uint32_t pfx = 0u;
+    int pfx_sh = sh;
+    bool first = true;
+    for (;;) {
+      const int nbits = first ? 11 : (pfx_sh < 11 ? pfx_sh : 11);
+      const int sel_sh = first ? sh : pfx_sh - nbits;
+      const uint32_t mask = (1u << nbits) - 1u;
+      __syncthreads();  // earlier readers of hist / wa / bc are done
+      hist[2 * tid] = 0u;
+      hist[2 * tid + 1] = (first && tid == kSelThreads - 1) ? nprot + npad : 0u;  // bin 2047
       __syncthreads();
-      for (int64_t i0 = a + tid; i0 < c; i0 += 4 * kSelThreads) {
-        uint32_t k4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t i = i0 + u * kSelThreads;
-          k4[u] = i < c ? key_at(i) : 0u;
+      for (int r = 0; r < nr; ++r) {
+        if (nr > 1) {
+          sv.load(r, key);
+          sv.rebase(key, kmn);
         }
+        if (first) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t i = i0 + u * kSelThreads;
-          if (i < c && (k4[u] & pmask) == prefix) atomicAdd(&hist[(k4[u] >> shf) & (nb - 1)], 1u);
+          for (int j = 0; j < kSelKpt; ++j) {
+            const uint32_t d = key[j] >> sh;  // protected and padding keys give >= 2047
+            if (d < 2047u) atomicAdd(&hist[d], 1u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < kSelKpt; ++j) {
+            const uint32_t v = key[j];
+            if ((v >> pfx_sh) == pfx) atomicAdd(&hist[(v >> sel_sh) & mask], 1u);
+          }
         }
       }
       __syncthreads();
-      // counts above each digit: thread t owns digits [per*t, per*t+per) from the top
-      const int per = nb / kSelThreads;  // 2 or 1
-      uint32_t mine = 0;
-      for (int e = 0; e < per; ++e) mine += hist[nb - 1 - (tid * per + e)];
+      // thread t owns bins 2047 - 2t (upper) and 2046 - 2t, counted from the top
+      const int d0 = 2047 - 2 * tid;
+      const uint32_t h0 = hist[d0], h1 = hist[d0 - 1];
+      const uint32_t mine = h0 + h1;
       uint32_t incl = mine;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const uint32_t y = __shfl_up(incl, off);
         if (lane >= off) incl += y;
       }
-      if (lane == 63) wt_def[wave] = incl;
+      if (lane == 63) wa[wave] = incl;
       __syncthreads();
-      wave_totals_scan(wt_def);
-      __syncthreads();
-      uint32_t above = wt_def[wave] + incl - mine;
-      for (int e = 0; e < per; ++e) {
-        const int dgt = nb - 1 - (tid * per + e);
-        const uint32_t cnt = hist[dgt];
-        if (above < need && above + cnt >= need) {
-          sh[0] = (uint32_t)dgt;
-          sh[1] = above;
-        }
-        above += cnt;
+      uint32_t above = incl - mine;
+      for (int w = 0; w < wave; ++w) above += wa[w];
+      if (above < need && above + h0 >= need) {
+        bc[0] = (uint32_t)d0;
+        bc[1] = above;
+      } else if (above + h0 < need && above + mine >= need) {
+        bc[0] = (uint32_t)(d0 - 1);
+        bc[1] = above + h0;
       }
       __syncthreads();
-      prefix |= sh[0] << shf;
-      pmask |= (uint32_t)(nb - 1) << shf;
-      need -= sh[1];
-      __syncthreads();
+      const uint32_t dsel = bc[0];
+      need -= bc[1];
+      pfx = first ? dsel : ((pfx << nbits) | dsel);
+      pfx_sh = sel_sh;
+      first = false;
+      if (pfx_sh == 0) break;
     }
-    thr = prefix;
-    rem = need;  // ties at the threshold still to take, in position order
+    thr = pfx;  // rebased
+    rem = need;
   }
-
-  // ordered emission: wave w walks [w * seg, (w + 1) * seg) in 64-position steps
-  const int64_t seg = ((N + kSelWaves - 1) / kSelWaves + 63) / 64 * 64;
-  const int64_t s0 = wave * seg;
-  const int64_t s1 = s0 + seg < N ? s0 + seg : N;
-  auto classify = [&](int64_t i, bool& def, bool& tie) {
-    def = false;
-    tie = false;
-    if (i < s1) {
-      if (i < a || i >= c || mode == 1) {
-        def = true;
-      } else if (mode == 2) {
-        const uint32_t k = key_at(i);
-        def = k > thr;
-        tie = k == thr;
-      }
+  // ordered emission, round by round
+  uint32_t Dr = 0u, Tr = 0u;  // kept-by-rank and tied keys before this round
+  const unsigned long long below = lanes_below(lane);
+  for (int r = 0; r < nr; ++r) {
+    if (nr > 1) {
+      sv.load(r, key);
+      if (rebased) sv.rebase(key, kmn);
     }
-  };
-  uint32_t n_def = 0, n_tie = 0;
-  for (int64_t base = s0; base < s1; base += 64) {
-    bool def, tie;
-    classify(base + lane, def, tie);
-    n_def += (uint32_t)__popcll(__ballot(def));
-    n_tie += (uint32_t)__popcll(__ballot(tie));
-  }
-  if (lane == 0) {
-    wt_def[wave] = n_def;
-    wt_tie[wave] = n_tie;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t tie_run = 0, out_run = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t ties = wt_tie[w];
-      const uint32_t take = tie_run >= rem ? 0u : (rem - tie_run < ties ? rem - tie_run : ties);
-      const uint32_t keep = wt_def[w] + take;
-      wt_tie[w] = tie_run;
-      wt_keep[w] = out_run;
-      tie_run += ties;
-      out_run += keep;
+    uint32_t nd = 0u, nt = 0u;  // per lane, then per wave
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      nd += (key[j] > thr && key[j] != kPad) ? 1u : 0u;
+      nt += key[j] == thr ? 1u : 0u;
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      nd += __shfl_xor(nd, off);
+      nt += __shfl_xor(nt, off);
+    }
+    __syncthreads();  // earlier readers of wa / wb are done
+    if (lane == 0) {
+      wa[wave] = nd;
+      wb[wave] = nt;
+    }
+    __syncthreads();
+    // lanes 0..15 take one wave's counts each: totals and this wave's prefix
+    const uint32_t x = lane < kSelWaves ? wa[lane] : 0u, y = lane < kSelWaves ? wb[lane] : 0u;
+    uint32_t xb = lane < wave ? x : 0u, yb = lane < wave ? y : 0u, dtot = x, ttot = y;
+#pragma unroll
+    for (int off = kSelWaves / 2; off >= 1; off >>= 1) {
+      xb += __shfl_xor(xb, off);
+      yb += __shfl_xor(yb, off);
+      dtot += __shfl_xor(dtot, off);
+      ttot += __shfl_xor(ttot, off);
+    }
+    uint32_t D = Dr + __builtin_amdgcn_readfirstlane(xb), Tt = Tr + __builtin_amdgcn_readfirstlane(yb);
+    dtot = __builtin_amdgcn_readfirstlane(dtot);
+    ttot = __builtin_amdgcn_readfirstlane(ttot);
+    const int p0 = sv.base(r);
+    uint32_t thw = thr;
+    asm volatile("" : "+v"(thw));  // keeps the counting compares from being reused here
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      const bool def = key[j] > thw && key[j] != kPad;
+      const bool tie = key[j] == thw;
+      const unsigned long long bd = __ballot(def), bt = __ballot(tie);
+      const uint32_t dr = (uint32_t)__popcll(bd & below), tr = (uint32_t)__popcll(bt & below);
+      const uint32_t tk = Tt + tr;  // tied keys before this one
+      uint32_t o = 0xffffffffu;
+      if (def) o = D + dr + (tk < rem ? tk : rem);
+      else if (tie && tk < rem) o = D + dr + tk;
+      if (o < (uint32_t)kept) out[o] = p0 + 64 * j;  // never past this sequence's slice
+      D += (uint32_t)__popcll(bd);
+      Tt += (uint32_t)__popcll(bt);
+    }
+    Dr += dtot;
+    Tr += ttot;
   }
-  __syncthreads();
-  uint32_t tie_before = wt_tie[wave], out_pos = wt_keep[wave];
-  for (int64_t base = s0; base < s1; base += 64) {
-    const int64_t i = base + lane;
-    bool def, tie;
-    classify(i, def, tie);
-    const unsigned long long tb = __ballot(tie);
-    const uint32_t rank = tie_before + (uint32_t)__popcll(tb & lanes_below(lane));
-    const bool keep = def || (tie && rank < rem);
-    const unsigned long long kb = __ballot(keep);
-    const uint32_t o = out_pos + (uint32_t)__popcll(kb & lanes_below(lane));
-    if (keep && o < (uint32_t)kept) out[o] = (int32_t)i;  // never past this sequence's slice
-    tie_before += (uint32_t)__popcll(tb);
-    out_pos += (uint32_t)__popcll(kb);
-  }
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ z,
-                                                             SeqTable st, int64_t T, int64_t Ktot,
-                                                             int n_sink, int n_recent,
-                                                             int32_t* __restrict__ idx) {
-  __shared__ uint32_t keys[kSelLdsKeys];
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wt_def[kSelWaves], wt_tie[kSelWaves], wt_keep[kSelWaves];
-  __shared__ uint32_t sh[2];
-  const int lh = blockIdx.y, b = blockIdx.x;
-  const int64_t N = st.N[b];
-  const float* zb = z + (int64_t)lh * T + st.cu[b];
-  int32_t* out = idx + (int64_t)lh * Ktot + st.ko[b];
-  const int64_t a = n_sink < N ? n_sink : N;
-  int64_t c = N - n_recent > 0 ? N - n_recent : 0;
-  if (c < a) c = a;
-  if (c - a <= kSelLdsKeys)
-    select_body<true>(zb, out, N, st.kept[b], n_sink, n_recent, keys, hist, wt_def, wt_tie,
-                      wt_keep, sh);
-  else
-    select_body<false>(zb, out, N, st.kept[b], n_sink, n_recent, keys, hist, wt_def, wt_tie,
-                       wt_keep, sh);
 }
 
 }  // namespace
@@ -420,22 +497,13 @@ hipError_t launch_head_stats(const float* s, const SeqTable& st, int L, int Hkv,
 hipError_t launch_refine(const float* s, const SeqTable& st, int L, int Hkv,
                          const double* head_stats, const float* beta_in, int pool, float gamma,
                          float beta_lo, float beta_hi, float r2, float* z, float* beta_out,
-                         float* beta_ws, hipStream_t stream) {
+                         hipStream_t stream) {
   int64_t T = 0;
   for (int b = 0; b < st.B; ++b) T += st.N[b];
-  const float* beta = beta_in;
-  hipError_t e;
-  if (!beta) {
-    const int threads = ((Hkv + 63) / 64) * 64;
-    hipLaunchKernelGGL(beta_kernel, dim3(L * st.B), dim3(threads), 0, stream, st, Hkv, head_stats,
-                       beta_lo, beta_hi, beta_ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    beta = beta_ws;
-  }
   const int nchunk = st.tile_off[st.B];
-  hipLaunchKernelGGL(refine_kernel, dim3(nchunk, L * Hkv), dim3(256), 0, stream, s, st, T, Hkv,
-                     pool / 2, gamma, r2, beta, z, beta_out);
+  hipLaunchKernelGGL(refine_kernel, dim3(nchunk, L * Hkv), dim3(kRefineThreads), 0, stream, s, st,
+                     T, Hkv, pool / 2, gamma, r2, beta_in, head_stats, beta_lo, beta_hi, z,
+                     beta_out);
   return hipGetLastError();
 }
 
