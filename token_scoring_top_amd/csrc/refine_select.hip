@@ -201,22 +201,23 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(
 // sequence).
 //
 // Layout: the sequence is cut into rounds of kSelRound positions; inside a
-// round wave w owns kSelKpt sub-blocks of 64 consecutive positions and lane l
-// holds position (w * kSelKpt + j) * 64 + l of sub-block j, so every load is a
-// fully coalesced 256-byte row and position order inside a sub-block is lane
-// order (ballots give in-order ranks).  A sequence of one round keeps its
+// round wave w owns kSelKpt rows of 64 consecutive positions and lane l holds
+// position (w * kSelKpt + j) * 64 + l of row j, so every load is a fully
+// coalesced 256-byte row and position order inside a row is lane order
+// (ballots and mbcnt give in-order ranks).  A sequence of one round keeps its
 // keys in registers through every pass; longer ones reload each round from L2.
 //
-// Keys: order-preserving 32-bit images of z (NaN lowest, -0 == +0), at most
-// 0xff800000 (+inf).  Protected positions get kProt, above every real key, and
-// positions past the end get kPad; neither is ever a candidate.  Once the
-// candidates' range [kmin, kmax] is known, candidate keys are rebased to
-// v = key - kmin in place.  Pass 1 bins v >> sh with the smallest shift that
-// fits the range into 2047 bins (about 2047 occupied bins, few LDS-atomic
-// collisions), protected and padding keys counted in bin 2047; further passes
-// resolve the remaining low bits 11 at a time inside the chosen bin.  The
-// result is (thr, rem): every key above thr is kept, plus the first rem keys
-// equal to thr in position order.
+// Keys: when no candidate is negative, -0 or NaN (scores are sums of
+// probabilities) the raw fp32 bits already order the values and are used as
+// they are; otherwise each value is mapped to an order-preserving key (NaN
+// lowest, -0 == +0).  Protected positions get kProt and positions past the
+// end kPad, above every real key; only the waves whose rows touch the
+// protected windows or the end pay for that.  Candidate keys are rebased to
+// key - kmin; pass 1 bins them with the smallest shift that fits their range
+// into 2047 bins (few LDS-atomic collisions), protected and padding keys
+// counted in bin 2047; later passes resolve the remaining low bits 11 at a
+// time inside the chosen bin.  The result is (thr, rem): every key above thr
+// is kept, plus the first rem keys equal to thr in position order.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -225,15 +226,15 @@ constexpr int kSelRound = kSelThreads * kSelKpt;
 constexpr uint32_t kProt = 0xffffffffu;
 constexpr uint32_t kPad = 0xfffffffeu;
 
-__device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t u = __float_as_uint(v);
+__device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
+  const float v = __uint_as_float(u);
   u = u == 0x80000000u ? 0u : u;                            // -0 == +0
   const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return v != v ? 0u : k;                                   // NaN ranks below everything
 }
 
-__device__ __forceinline__ unsigned long long lanes_below(int lane) {
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+__device__ __forceinline__ uint32_t rank_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -254,43 +255,482 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+typedef const __attribute__((address_space(1))) uint32_t* gbits;  // global memory
+
 struct SelView {
-  const float* zb;
+  gbits zb;  // bits of z
   int N, a, c, wave, lane;
-  __device__ __forceinline__ int base(int r) const {
-    return r * kSelRound + wave * (64 * kSelKpt) + lane;
+  __device__ __forceinline__ int seg0(int r) const {
+    return r * kSelRound + wave * (64 * kSelKpt);
   }
-  // keys of round r; a position past N reads a clamped address and gets kPad
-  __device__ __forceinline__ void load(int r, uint32_t (&key)[kSelKpt]) const {
-    const int p0 = base(r);
-    float v[kSelKpt];
+  // rows of this wave in round r touch a protected window or the end
+  __device__ __forceinline__ bool edge(int r) const {
+    const int s0 = seg0(r);
+    return s0 < a || s0 + 64 * kSelKpt > c;
+  }
+  // raw bits of round r; on edge waves positions past N read a clamped address
+  __device__ __forceinline__ void load_raw(int r, uint32_t (&key)[kSelKpt]) const {
+    const int p0 = seg0(r) + lane;
+    if (edge(r)) {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        const int p = p0 + 64 * j;
+        key[j] = zb[p < N ? p : N - 1];
+      }
+    } else {
+      const gbits zr = zb + p0;
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) key[j] = zr[64 * j];
+    }
+  }
+  __device__ __forceinline__ void specials(int r, uint32_t (&key)[kSelKpt]) const {
+    const int p0 = seg0(r) + lane;
 #pragma unroll
     for (int j = 0; j < kSelKpt; ++j) {
       const int p = p0 + 64 * j;
-      v[j] = zb[p < N ? p : N - 1];
-    }
-#pragma unroll
-    for (int j = 0; j < kSelKpt; ++j) {
-      const int p = p0 + 64 * j;
-      const uint32_t k = order_key(v[j]);
-      const uint32_t kp = (p < a || p >= c) ? kProt : k;
-      key[j] = p >= N ? kPad : kp;
+      key[j] = p >= N ? kPad : ((p < a || p >= c) ? kProt : key[j]);
     }
   }
-  // rebase candidate keys to key - kmin (special keys unchanged)
-  __device__ __forceinline__ void rebase(uint32_t (&key)[kSelKpt], uint32_t kmn) const {
+  // keys of round r, rebased by kmn
+  __device__ __forceinline__ void load(int r, uint32_t (&key)[kSelKpt], bool conv,
+                                       uint32_t kmn) const {
+    load_raw(r, key);
+    if (conv) {
 #pragma unroll
-    for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
+      for (int j = 0; j < kSelKpt; ++j) key[j] = order_key_bits(key[j]);
+    }
+    if (edge(r)) {
+      specials(r, key);
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) key[j] -= kmn;
+    }
   }
 };
+
+// Block-wide min and max of per-lane values and OR of a per-lane flag.
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t& fl,
+                                             uint32_t* wa, uint32_t* wb, uint32_t* wc, int wave,
+                                             int lane) {
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  fl = wave_max_u32(fl);
+  __syncthreads();  // earlier readers of wa / wb / wc are done
+  if (lane == 0) {
+    wa[wave] = mn;
+    wb[wave] = mx;
+    wc[wave] = fl;
+  }
+  __syncthreads();
+  const uint32_t x = lane < kSelWaves ? wa[lane] : 0xffffffffu;
+  const uint32_t y = lane < kSelWaves ? wb[lane] : 0u;
+  const uint32_t f = lane < kSelWaves ? wc[lane] : 0u;
+  mn = __builtin_amdgcn_readfirstlane(wave_min_u32(x));
+  mx = __builtin_amdgcn_readfirstlane(wave_max_u32(y));
+  fl = __builtin_amdgcn_readfirstlane(wave_max_u32(f));
+}
+
+constexpr int kCandCap = 8192;   // keys of the threshold bin held in LDS
+constexpr int kFastRounds = 16;  // sequences up to 16 rounds take the fast path
+
+struct SelSmem {
+  uint32_t hist[4096];
+  uint32_t ckey[kCandCap];
+  int32_t cpos[kCandCap];
+  uint32_t rw_def[kFastRounds * kSelWaves];  // per (round, wave): keys above thr, then prefix
+  uint32_t rw_tie[kFastRounds * kSelWaves];  // per (round, wave): keys equal to thr, then prefix
+  uint32_t wa[kSelWaves], wb[kSelWaves], wc[kSelWaves];
+  uint32_t bc[2];
+  uint32_t ncand;
+};
+
+// Bin of hist[0 .. 1024 * kPer) holding the need-th largest count from the
+// top, and the count strictly above it; thread t owns bins
+// 1024 * kPer - 1 - kPer * t downwards.  Block-uniform results.
+template <int kPer>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t need, SelSmem& sm, int tid,
+                                         int lane, int wave, uint32_t& d, uint32_t& above_d) {
+  const int top = 1024 * kPer - 1 - kPer * tid;
+  uint32_t h[kPer], mine = 0u;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    h[e] = hist[top - e];
+    mine += h[e];
+  }
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sm.wa[wave] = incl;
+  __syncthreads();
+  uint32_t above = incl - mine;
+  for (int w = 0; w < wave; ++w) above += sm.wa[w];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (above < need && above + h[e] >= need) {
+      sm.bc[0] = (uint32_t)(top - e);
+      sm.bc[1] = above;
+    }
+    above += h[e];
+  }
+  __syncthreads();
+  d = sm.bc[0];
+  above_d = sm.bc[1];
+}
+
+// Ordered writes of one round: keys above thr, then the first rem keys equal
+// to thr, ranked from D and Tt (keys above / equal to thr before this wave's
+// rows).  Keys in registers, specials applied.
+__device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool edge, uint32_t thr,
+                                           uint32_t rem, uint32_t D, uint32_t Tt, int p0, int kept,
+                                           int32_t* __restrict__ out) {
+  uint32_t thw = thr;
+  asm volatile("" : "+v"(thw));  // keeps earlier compares against thr from being reused
+#pragma unroll
+  for (int j = 0; j < kSelKpt; ++j) {
+    const uint32_t k = key[j];
+    const bool def = edge ? (k > thw && k != kPad) : (k > thw);
+    const unsigned long long bd = __ballot(def);
+    const unsigned long long bt = __ballot(k == thw);
+    if (bt == 0ull) {
+      // no key of this row equals thr: kept ranks are those of the keys above it
+      const uint32_t o = D + rank_below(bd) + (Tt < rem ? Tt : rem);
+      if (def && o < (uint32_t)kept) out[o] = p0 + 64 * j;
+    } else {
+      const uint32_t tk = Tt + rank_below(bt);  // tied keys before this one
+      uint32_t o = 0xffffffffu;
+      if (def) o = D + rank_below(bd) + (tk < rem ? tk : rem);
+      else if (k == thw && tk < rem) o = D + rank_below(bd) + tk;
+      if (o < (uint32_t)kept) out[o] = p0 + 64 * j;  // never past this sequence's slice
+    }
+    D += (uint32_t)__popcll(bd);
+    Tt += (uint32_t)__popcll(bt);
+  }
+}
+
+// Fast path for sequences whose candidates are all +0, positive or +inf (the
+// raw bits order them): one histogram sweep over the top 12 bits, one sweep
+// that counts the keys above the threshold bin per (round, wave) and copies
+// the bin's keys to LDS, the remaining 20 bits resolved on that copy, and one
+// write sweep.  Returns false, having written nothing, when a candidate
+// needs an order key, the bin is larger than kCandCap or the sequence is
+// longer than kFastRounds rounds.
+__device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int nr, uint32_t nprot, uint32_t npad,
+                            int kept, int32_t* __restrict__ out, int tid, int lane, int wave) {
+  if (nr > kFastRounds) return false;
+  const int N = sv.N, a = sv.a, c = sv.c;
+  uint32_t key[kSelKpt];
+  for (int i = tid; i < 4096; i += kSelThreads) sm.hist[i] = i == 4095 ? nprot + npad : 0u;
+  __syncthreads();
+  // raw bits above +inf's (0x7f800000) belong to a NaN or a negative value
+  uint32_t bmax = 0u;
+  for (int r = 0; r < nr; ++r) {
+    sv.load_raw(r, key);
+    if (sv.edge(r)) {
+      const int p0 = sv.seg0(r) + lane;
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        const int p = p0 + 64 * j;
+        const bool cand = p < N && p >= a && p < c;
+        bmax = (cand && key[j] > bmax) ? key[j] : bmax;
+        key[j] = p >= N ? kPad : (cand ? key[j] : kProt);
+        if (cand) atomicAdd(&sm.hist[key[j] >> 20], 1u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        bmax = key[j] > bmax ? key[j] : bmax;
+        atomicAdd(&sm.hist[key[j] >> 20], 1u);
+      }
+    }
+  }
+  bmax = wave_max_u32(bmax);
+  if (lane == 0) sm.wc[wave] = bmax;
+  __syncthreads();
+  bmax = __builtin_amdgcn_readfirstlane(wave_max_u32(lane < kSelWaves ? sm.wc[lane] : 0u));
+  if (bmax > 0x7f800000u) return false;
+  // counted from the top: protected keys and padding sit in bin 4095
+  uint32_t need = (uint32_t)kept + npad, d1, above;
+  find_bin<4>(sm.hist, need, sm, tid, lane, wave, d1, above);
+  need -= above;
+  const uint32_t c1 = sm.hist[d1];
+  if (c1 > (uint32_t)kCandCap) return false;
+
+  // sweep 2: keys above bin d1 per (round, wave); keys of bin d1 to LDS
+  if (tid == 0) sm.ncand = 0u;
+  __syncthreads();
+  for (int r = 0; r < nr; ++r) {
+    const bool edge = sv.edge(r);
+    if (nr > 1) {
+      sv.load_raw(r, key);
+      if (edge) sv.specials(r, key);
+    }
+    const int p0 = sv.seg0(r) + lane;
+    uint32_t nhi = 0u;
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      const uint32_t bin = key[j] >> 20;  // specials give 4095
+      nhi += (uint32_t)__popcll(__ballot(edge ? (bin > d1 && key[j] != kPad) : bin > d1));
+      if (bin == d1) {
+        const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+        sm.ckey[slot] = key[j];
+        sm.cpos[slot] = p0 + 64 * j;
+      }
+    }
+    if (lane == 0) sm.rw_def[r * kSelWaves + wave] = nhi;
+  }
+  // the bin's low 20 bits: 11, then 9, on the LDS copy
+  for (int i = tid; i < 2048; i += kSelThreads) sm.hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < (int)c1; i += kSelThreads) atomicAdd(&sm.hist[(sm.ckey[i] >> 9) & 2047u], 1u);
+  __syncthreads();
+  uint32_t da, db;
+  find_bin<2>(sm.hist, need, sm, tid, lane, wave, da, above);
+  need -= above;
+  for (int i = tid; i < 2048; i += kSelThreads) sm.hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < (int)c1; i += kSelThreads) {
+    const uint32_t k = sm.ckey[i];
+    if (((k >> 9) & 2047u) == da) atomicAdd(&sm.hist[k & 511u], 1u);
+  }
+  __syncthreads();
+  find_bin<2>(sm.hist, need, sm, tid, lane, wave, db, above);
+  need -= above;
+  const uint32_t thr = (d1 << 20) | (da << 9) | db;
+  const uint32_t rem = need;
+
+  // add the bin's keys above / equal to thr to the per-(round, wave) counts
+  for (int i = tid; i < nr * kSelWaves; i += kSelThreads) sm.rw_tie[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < (int)c1; i += kSelThreads) {
+    const uint32_t k = sm.ckey[i];
+    const int p = sm.cpos[i];
+    const int rw = (p / kSelRound) * kSelWaves + (p % kSelRound) / (64 * kSelKpt);
+    if (k > thr) atomicAdd(&sm.rw_def[rw], 1u);
+    else if (k == thr) atomicAdd(&sm.rw_tie[rw], 1u);
+  }
+  __syncthreads();
+  // exclusive prefix over (round, wave) in position order, by wave 0
+  if (wave == 0) {
+    uint32_t Dp = 0u, Tp = 0u;
+    for (int base = 0; base < nr * kSelWaves; base += 64) {
+      const int i = base + lane;
+      const uint32_t x = i < nr * kSelWaves ? sm.rw_def[i] : 0u;
+      const uint32_t y = i < nr * kSelWaves ? sm.rw_tie[i] : 0u;
+      uint32_t xi = x, yi = y;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t xs = __shfl_up(xi, off), ys = __shfl_up(yi, off);
+        if (lane >= off) {
+          xi += xs;
+          yi += ys;
+        }
+      }
+      if (i < nr * kSelWaves) {
+        sm.rw_def[i] = Dp + xi - x;
+        sm.rw_tie[i] = Tp + yi - y;
+      }
+      Dp += __shfl(xi, 63);
+      Tp += __shfl(yi, 63);
+    }
+  }
+  __syncthreads();
+
+  // sweep 3: ordered writes
+  for (int r = 0; r < nr; ++r) {
+    const bool edge = sv.edge(r);
+    if (nr > 1) {
+      sv.load_raw(r, key);
+      if (edge) sv.specials(r, key);
+    }
+    const uint32_t D = sm.rw_def[r * kSelWaves + wave], Tt = sm.rw_tie[r * kSelWaves + wave];
+    emit_round(key, edge, thr, rem, D, Tt, sv.seg0(r) + lane, kept, out);
+  }
+  return true;
+}
+
+// General path: order keys when needed, a first pass binned over the
+// candidates' own key range, further radix passes over every key.
+__device__ __noinline__ void select_generic(const SelView& sv, SelSmem& sm, int nr, uint32_t nprot,
+                               uint32_t npad, int kept, int32_t* __restrict__ out, int tid,
+                               int lane, int wave) {
+  const int N = sv.N, a = sv.a, c = sv.c;
+
+  // pass 0: candidate range in raw-bit space, and whether raw bits order them
+  // (their largest raw bits above +inf's mean a NaN or a negative value)
+  uint32_t key[kSelKpt];
+  uint32_t mn = 0xffffffffu, mx = 0u, bad = 0u;
+  for (int r = 0; r < nr; ++r) {
+    sv.load_raw(r, key);
+    if (sv.edge(r)) {
+      const int p0 = sv.seg0(r) + lane;
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        const int p = p0 + 64 * j;
+        const bool cand = p < N && p >= a && p < c;
+        bad = (cand && key[j] > bad) ? key[j] : bad;
+        key[j] = p >= N ? kPad : (cand ? key[j] : kProt);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) bad = key[j] > bad ? key[j] : bad;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      mn = key[j] < mn ? key[j] : mn;        // specials are above every candidate
+      const uint32_t k2 = key[j] + 2u;       // specials wrap to 0 and 1
+      mx = k2 > mx ? k2 : mx;
+    }
+  }
+  block_minmax(mn, mx, bad, sm.wa, sm.wb, sm.wc, wave, lane);
+  const bool conv = bad > 0x7f800000u;  // a NaN or a negative value among the candidates
+  if (conv) {  // order-preserving keys instead of raw bits (not yet rebased)
+    mn = 0xffffffffu;
+    mx = 0u;
+    uint32_t dummy = 0u;
+    for (int r = 0; r < nr; ++r) {
+      sv.load(r, key, true, 0u);
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        mn = key[j] < mn ? key[j] : mn;
+        const uint32_t k2 = key[j] + 2u;
+        mx = k2 > mx ? k2 : mx;
+      }
+    }
+    block_minmax(mn, mx, dummy, sm.wa, sm.wb, sm.wc, wave, lane);
+  }
+  const uint32_t kmn = mn;
+  const uint32_t range = (mx - 2u) - mn;  // <= 0xff800000, so sh <= 21
+  if (nr == 1) {  // rebase the keys held in registers
+    if (sv.edge(0)) {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) key[j] -= kmn;
+    }
+  }
+  int sh = 0;
+  while ((range >> sh) > 2046u) ++sh;
+
+  // radix passes; counted from the top, protected keys and padding in bin 2047
+  uint32_t need = (uint32_t)kept + npad;
+  uint32_t pfx = 0u;
+  int pfx_sh = sh;
+  bool first = true;
+  for (;;) {
+    const int nbits = first ? 11 : (pfx_sh < 11 ? pfx_sh : 11);
+    const int sel_sh = first ? sh : pfx_sh - nbits;
+    const uint32_t mask = (1u << nbits) - 1u;
+    __syncthreads();  // earlier readers of hist / wa / bc are done
+    sm.hist[2 * tid] = 0u;
+    sm.hist[2 * tid + 1] = (first && tid == kSelThreads - 1) ? nprot + npad : 0u;  // bin 2047
+    __syncthreads();
+    for (int r = 0; r < nr; ++r) {
+      if (nr > 1) sv.load(r, key, conv, kmn);
+      if (first) {
+        if (sv.edge(r)) {
+#pragma unroll
+          for (int j = 0; j < kSelKpt; ++j) {
+            const uint32_t d = key[j] >> sh;  // protected and padding keys give >= 2047
+            if (d < 2047u) atomicAdd(&sm.hist[d], 1u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < kSelKpt; ++j) atomicAdd(&sm.hist[key[j] >> sh], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j) {
+          const uint32_t v = key[j];
+          if ((v >> pfx_sh) == pfx) atomicAdd(&sm.hist[(v >> sel_sh) & mask], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // thread t owns bins 2047 - 2t (upper) and 2046 - 2t, counted from the top
+    const int d0 = 2047 - 2 * tid;
+    const uint32_t h0 = sm.hist[d0], h1 = sm.hist[d0 - 1];
+    const uint32_t mine = h0 + h1;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) sm.wa[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - mine;
+    for (int w = 0; w < wave; ++w) above += sm.wa[w];
+    if (above < need && above + h0 >= need) {
+      sm.bc[0] = (uint32_t)d0;
+      sm.bc[1] = above;
+    } else if (above + h0 < need && above + mine >= need) {
+      sm.bc[0] = (uint32_t)(d0 - 1);
+      sm.bc[1] = above + h0;
+    }
+    __syncthreads();
+    const uint32_t dsel = sm.bc[0];
+    need -= sm.bc[1];
+    pfx = first ? dsel : ((pfx << nbits) | dsel);
+    pfx_sh = sel_sh;
+    first = false;
+    if (pfx_sh == 0) break;
+  }
+  const uint32_t thr = pfx;  // rebased; every candidate key is below kPad
+  const uint32_t rem = need;
+
+  // ordered emission, round by round
+  uint32_t Dr = 0u, Tr = 0u;  // keys above thr and keys equal to thr before this round
+  for (int r = 0; r < nr; ++r) {
+    if (nr > 1) sv.load(r, key, conv, kmn);
+    const bool edge = sv.edge(r);
+    uint32_t nd = 0u, nt = 0u;
+    if (edge) {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        nd += (uint32_t)__popcll(__ballot(key[j] > thr && key[j] != kPad));
+        nt += (uint32_t)__popcll(__ballot(key[j] == thr));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelKpt; ++j) {
+        nd += (uint32_t)__popcll(__ballot(key[j] > thr));
+        nt += (uint32_t)__popcll(__ballot(key[j] == thr));
+      }
+    }
+    __syncthreads();  // earlier readers of wa / wb are done
+    if (lane == 0) {
+      sm.wa[wave] = nd;
+      sm.wb[wave] = nt;
+    }
+    __syncthreads();
+    // lanes 0..15 take one wave's counts each: totals and this wave's prefix
+    const uint32_t x = lane < kSelWaves ? sm.wa[lane] : 0u, y = lane < kSelWaves ? sm.wb[lane] : 0u;
+    uint32_t xb = lane < wave ? x : 0u, yb = lane < wave ? y : 0u, dtot = x, ttot = y;
+#pragma unroll
+    for (int off = kSelWaves / 2; off >= 1; off >>= 1) {
+      xb += __shfl_xor(xb, off);
+      yb += __shfl_xor(yb, off);
+      dtot += __shfl_xor(dtot, off);
+      ttot += __shfl_xor(ttot, off);
+    }
+    emit_round(key, edge, thr, rem, Dr + __builtin_amdgcn_readfirstlane(xb),
+               Tr + __builtin_amdgcn_readfirstlane(yb), sv.seg0(r) + lane, kept, out);
+    Dr += __builtin_amdgcn_readfirstlane(dtot);
+    Tr += __builtin_amdgcn_readfirstlane(ttot);
+  }
+}
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ z,
                                                              SeqTable st, int64_t T, int64_t Ktot,
                                                              int n_sink, int n_recent,
                                                              int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wa[kSelWaves], wb[kSelWaves];
-  __shared__ uint32_t bc[2];
+  __shared__ SelSmem sm;
   const int lh = blockIdx.y, b = blockIdx.x;
   const int N = (int)st.N[b];
   const int kept = (int)st.kept[b];
@@ -301,179 +741,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   int c = N - n_recent > 0 ? N - n_recent : 0;
   if (c < a) c = a;
   const uint32_t nprot = (uint32_t)(a + (N - c));
-  const SelView sv{z + (int64_t)lh * T + st.cu[b], N, a, c, wave, lane};
   int32_t* out = idx + (int64_t)lh * Ktot + st.ko[b];
+
+  // all positions kept, or only the protected ones: no keys needed
+  if ((uint32_t)kept >= (uint32_t)N || (uint32_t)kept <= nprot) {
+    const bool all = (uint32_t)kept >= (uint32_t)N;
+    for (int p = tid; p < N; p += kSelThreads) {
+      if (all) {
+        out[p] = p;
+      } else if (p < a) {
+        out[p] = p;
+      } else if (p >= c && a + (p - c) < kept) {
+        out[a + (p - c)] = p;
+      }
+    }
+    return;
+  }
+  const SelView sv{(gbits)(z + (int64_t)lh * T + st.cu[b]), N, a, c, wave, lane};
   const int nr = (N + kSelRound - 1) / kSelRound;
   const uint32_t npad = (uint32_t)(nr * kSelRound - N);
-
-  uint32_t key[kSelKpt];
-  sv.load(0, key);
-
-  // keep rule: key > thr (kPad excluded), or key == thr among the first rem
-  // such keys in position order; keys are rebased when a select ran
-  uint32_t thr, rem, kmn = 0u;
-  bool rebased = false;
-  if ((uint32_t)kept >= (uint32_t)N) {
-    thr = 0u;
-    rem = (uint32_t)N;
-  } else if ((uint32_t)kept <= nprot) {
-    thr = kProt;
-    rem = (uint32_t)kept;
-  } else {
-    // range of the candidate keys
-    uint32_t mn = kPad, mx = 0u;
-    for (int r = 0; r < nr; ++r) {
-      if (nr > 1) sv.load(r, key);
-#pragma unroll
-      for (int j = 0; j < kSelKpt; ++j) {
-        const uint32_t k = key[j];
-        mn = k < mn ? k : mn;                    // specials are >= kPad
-        mx = (k < kPad && k > mx) ? k : mx;
-      }
-    }
-    mn = wave_min_u32(mn);
-    mx = wave_max_u32(mx);
-    if (lane == 0) {
-      wa[wave] = mn;
-      wb[wave] = mx;
-    }
-    __syncthreads();
-    mn = kPad;
-    mx = 0u;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      mn = wa[w] < mn ? wa[w] : mn;
-      mx = wb[w] > mx ? wb[w] : mx;
-    }
-    kmn = mn;
-    rebased = true;
-    const uint32_t range = mx - mn;  // <= 0xff800000, so sh <= 21
-    int sh = 0;
-    while ((range >> sh) > 2046u) ++sh;
-    if (nr == 1) sv.rebase(key, kmn);
-
-    // counted from the top: protected keys and padding sit in bin 2047
-    uint32_t need = (uint32_t)kept + npad;
-    uint32_t pfx = 0u;
-    int pfx_sh = sh;
-    bool first = true;
-    for (;;) {
-      const int nbits = first ? 11 : (pfx_sh < 11 ? pfx_sh : 11);
-      const int sel_sh = first ? sh : pfx_sh - nbits;
-      const uint32_t mask = (1u << nbits) - 1u;
-      __syncthreads();  // earlier readers of hist / wa / bc are done
-      hist[2 * tid] = 0u;
-      hist[2 * tid + 1] = (first && tid == kSelThreads - 1) ? nprot + npad : 0u;  // bin 2047
-      __syncthreads();
-      for (int r = 0; r < nr; ++r) {
-        if (nr > 1) {
-          sv.load(r, key);
-          sv.rebase(key, kmn);
-        }
-        if (first) {
-#pragma unroll
-          for (int j = 0; j < kSelKpt; ++j) {
-            const uint32_t d = key[j] >> sh;  // protected and padding keys give >= 2047
-            if (d < 2047u) atomicAdd(&hist[d], 1u);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < kSelKpt; ++j) {
-            const uint32_t v = key[j];
-            if ((v >> pfx_sh) == pfx) atomicAdd(&hist[(v >> sel_sh) & mask], 1u);
-          }
-        }
-      }
-      __syncthreads();
-      // thread t owns bins 2047 - 2t (upper) and 2046 - 2t, counted from the top
-      const int d0 = 2047 - 2 * tid;
-      const uint32_t h0 = hist[d0], h1 = hist[d0 - 1];
-      const uint32_t mine = h0 + h1;
-      uint32_t incl = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      if (lane == 63) wa[wave] = incl;
-      __syncthreads();
-      uint32_t above = incl - mine;
-      for (int w = 0; w < wave; ++w) above += wa[w];
-      if (above < need && above + h0 >= need) {
-        bc[0] = (uint32_t)d0;
-        bc[1] = above;
-      } else if (above + h0 < need && above + mine >= need) {
-        bc[0] = (uint32_t)(d0 - 1);
-        bc[1] = above + h0;
-      }
-      __syncthreads();
-      const uint32_t dsel = bc[0];
-      need -= bc[1];
-      pfx = first ? dsel : ((pfx << nbits) | dsel);
-      pfx_sh = sel_sh;
-      first = false;
-      if (pfx_sh == 0) break;
-    }
-    thr = pfx;  // rebased
-    rem = need;
-  }
-  // ordered emission, round by round
-  uint32_t Dr = 0u, Tr = 0u;  // kept-by-rank and tied keys before this round
-  const unsigned long long below = lanes_below(lane);
-  for (int r = 0; r < nr; ++r) {
-    if (nr > 1) {
-      sv.load(r, key);
-      if (rebased) sv.rebase(key, kmn);
-    }
-    uint32_t nd = 0u, nt = 0u;  // per lane, then per wave
-#pragma unroll
-    for (int j = 0; j < kSelKpt; ++j) {
-      nd += (key[j] > thr && key[j] != kPad) ? 1u : 0u;
-      nt += key[j] == thr ? 1u : 0u;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      nd += __shfl_xor(nd, off);
-      nt += __shfl_xor(nt, off);
-    }
-    __syncthreads();  // earlier readers of wa / wb are done
-    if (lane == 0) {
-      wa[wave] = nd;
-      wb[wave] = nt;
-    }
-    __syncthreads();
-    // lanes 0..15 take one wave's counts each: totals and this wave's prefix
-    const uint32_t x = lane < kSelWaves ? wa[lane] : 0u, y = lane < kSelWaves ? wb[lane] : 0u;
-    uint32_t xb = lane < wave ? x : 0u, yb = lane < wave ? y : 0u, dtot = x, ttot = y;
-#pragma unroll
-    for (int off = kSelWaves / 2; off >= 1; off >>= 1) {
-      xb += __shfl_xor(xb, off);
-      yb += __shfl_xor(yb, off);
-      dtot += __shfl_xor(dtot, off);
-      ttot += __shfl_xor(ttot, off);
-    }
-    uint32_t D = Dr + __builtin_amdgcn_readfirstlane(xb), Tt = Tr + __builtin_amdgcn_readfirstlane(yb);
-    dtot = __builtin_amdgcn_readfirstlane(dtot);
-    ttot = __builtin_amdgcn_readfirstlane(ttot);
-    const int p0 = sv.base(r);
-    uint32_t thw = thr;
-    asm volatile("" : "+v"(thw));  // keeps the counting compares from being reused here
-#pragma unroll
-    for (int j = 0; j < kSelKpt; ++j) {
-      const bool def = key[j] > thw && key[j] != kPad;
-      const bool tie = key[j] == thw;
-      const unsigned long long bd = __ballot(def), bt = __ballot(tie);
-      const uint32_t dr = (uint32_t)__popcll(bd & below), tr = (uint32_t)__popcll(bt & below);
-      const uint32_t tk = Tt + tr;  // tied keys before this one
-      uint32_t o = 0xffffffffu;
-      if (def) o = D + dr + (tk < rem ? tk : rem);
-      else if (tie && tk < rem) o = D + dr + tk;
-      if (o < (uint32_t)kept) out[o] = p0 + 64 * j;  // never past this sequence's slice
-      D += (uint32_t)__popcll(bd);
-      Tt += (uint32_t)__popcll(bt);
-    }
-    Dr += dtot;
-    Tr += ttot;
+  if (!select_fast(sv, sm, nr, nprot, npad, kept, out, tid, lane, wave)) {
+    __syncthreads();  // the fast path's readers of LDS are done
+    select_generic(sv, sm, nr, nprot, npad, kept, out, tid, lane, wave);
   }
 }
 
