@@ -1,6 +1,7 @@
 """Benchmark of the per-head KV retention path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # 1 GiB device copies, for counter scaling
 
 One step = the whole prefill path over one batch of synthetic input already
 resident in HBM: hubkv_score -> hubkv_refine -> hubkv_select -> hubkv_compact
@@ -27,6 +28,40 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+COPY_BYTES = 1 << 30         # size of one calibration copy
+
+# HBM bytes per launch of the score op (all of its kernels) on the
+# Llama-2-7B-shaped layer, from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
+# by the same counter over a plain 1 GiB device copy (`bench.py
+# --copy-calibration`).  Valid only for the score source they were taken on.
+SCORE_TRAFFIC = {"sha256": "b4f459670f6535fcd2bdc6a663acfc7fa9d06d03e99ff172af96996110e95449", "workload": 2,
+                 "fetch_bytes": 546507634, "write_bytes": 4858880}
+
+
+def _score_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("score.hip", "internal.hpp"):
+        with open(os.path.join(ROOT, "token_scoring_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def copy_calibration(reps: int = 5) -> int:
+    """Plain device-to-device copies of COPY_BYTES, for scaling HBM counters."""
+    import torch
+    assert torch.cuda.is_available(), "copy calibration needs a GPU"
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes": COPY_BYTES, "reps": reps, "GBs": 2 * COPY_BYTES / dt / 1e9}))
+    return 0
 
 
 def _cores() -> int:
@@ -65,6 +100,7 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
@@ -72,6 +108,9 @@ def main(argv=None):
               "would each run this same kernel chain on their own share of heads.",
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch
@@ -147,6 +186,10 @@ def main(argv=None):
 
     nb = op_bytes(w, Ksum, elem)
     dom = max(op_ms, key=op_ms.get)
+    traffic = None
+    if (dom == "score" and SCORE_TRAFFIC is not None and SCORE_TRAFFIC["workload"] == w.wid
+            and SCORE_TRAFFIC["sha256"] == _score_source_sha()):
+        traffic = SCORE_TRAFFIC["fetch_bytes"] + SCORE_TRAFFIC["write_bytes"]
     ach = nb[dom] / (op_ms[dom] / 1e3) / 1e9
     rsc_bytes = nb["refine"] + nb["select"] + nb["compact"]
     rsc_ms = op_ms["refine"] + op_ms["select"] + op_ms["compact"]
@@ -192,7 +235,7 @@ def main(argv=None):
                    "n_sink": w.n_sink, "n_recent": w.n_recent, "kept_per_head": int(Ksum),
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": dom,
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "op": dom,
                      "kernels": kernels[dom], "algorithmic_bytes": nb[dom]},
         "ops_ms": op_ms,
         "refine_select_compact": {"ms": rsc_ms, "bytes": rsc_bytes,

@@ -413,46 +413,66 @@ __device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool 
 }
 
 // Fast path for sequences whose candidates are all +0, positive or +inf (the
-// raw bits order them): one histogram sweep over the top 12 bits, one sweep
-// that counts the keys above the threshold bin per (round, wave) and copies
-// the bin's keys to LDS, the remaining 20 bits resolved on that copy, and one
-// write sweep.  Returns false, having written nothing, when a candidate
-// needs an order key, the bin is larger than kCandCap or the sequence is
-// longer than kFastRounds rounds.
-__device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int nr, uint32_t nprot, uint32_t npad,
-                            int kept, int32_t* __restrict__ out, int tid, int lane, int wave) {
+// raw bits order them).  Sweep 0 finds the candidates' bit range; sweep 1
+// bins the rebased bits with the smallest shift that fits that range into
+// 4095 bins (bin 4095 holds protected and padding keys); sweep 2 counts the
+// keys above the threshold bin per (round, wave) and copies the bin's keys to
+// LDS, where the remaining low bits are resolved; sweep 3 writes.  Returns
+// false, having written nothing, when a candidate needs an order key, the bin
+// is larger than kCandCap or the sequence is longer than kFastRounds rounds.
+__device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int nr, uint32_t nprot,
+                                            uint32_t npad, int kept, int32_t* __restrict__ out,
+                                            int tid, int lane, int wave) {
   if (nr > kFastRounds) return false;
   const int N = sv.N, a = sv.a, c = sv.c;
   uint32_t key[kSelKpt];
-  for (int i = tid; i < 4096; i += kSelThreads) sm.hist[i] = i == 4095 ? nprot + npad : 0u;
-  __syncthreads();
-  // raw bits above +inf's (0x7f800000) belong to a NaN or a negative value
-  uint32_t bmax = 0u;
+  // sweep 0: range of the candidates' raw bits; bits above +inf's
+  // (0x7f800000) belong to a NaN or a negative value
+  uint32_t mn = 0xffffffffu, mx = 0u;
   for (int r = 0; r < nr; ++r) {
     sv.load_raw(r, key);
-    if (sv.edge(r)) {
-      const int p0 = sv.seg0(r) + lane;
+    if (sv.edge(r)) sv.specials(r, key);
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      mn = key[j] < mn ? key[j] : mn;   // specials are above every candidate
+      const uint32_t k2 = key[j] + 2u;  // specials wrap to 0 and 1
+      mx = k2 > mx ? k2 : mx;
+    }
+  }
+  uint32_t unused = 0u;
+  block_minmax(mn, mx, unused, sm.wa, sm.wb, sm.wc, wave, lane);
+  mx -= 2u;
+  if (mx > 0x7f800000u) return false;
+  const uint32_t kmn = mn, range = mx - mn;
+  int sh = 0;
+  while ((range >> sh) > 4094u) ++sh;
+
+  // sweep 1: histogram of the rebased bits
+  for (int i = tid; i < 4096; i += kSelThreads) sm.hist[i] = i == 4095 ? nprot + npad : 0u;
+  __syncthreads();
+  for (int r = 0; r < nr; ++r) {
+    const bool edge = sv.edge(r);
+    if (nr > 1) {
+      sv.load_raw(r, key);
+      if (edge) sv.specials(r, key);
+    }
+    if (edge) {
 #pragma unroll
       for (int j = 0; j < kSelKpt; ++j) {
-        const int p = p0 + 64 * j;
-        const bool cand = p < N && p >= a && p < c;
-        bmax = (cand && key[j] > bmax) ? key[j] : bmax;
-        key[j] = p >= N ? kPad : (cand ? key[j] : kProt);
-        if (cand) atomicAdd(&sm.hist[key[j] >> 20], 1u);
+        if (key[j] < kPad) {
+          key[j] -= kmn;
+          atomicAdd(&sm.hist[key[j] >> sh], 1u);
+        }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kSelKpt; ++j) {
-        bmax = key[j] > bmax ? key[j] : bmax;
-        atomicAdd(&sm.hist[key[j] >> 20], 1u);
+        key[j] -= kmn;
+        atomicAdd(&sm.hist[key[j] >> sh], 1u);
       }
     }
   }
-  bmax = wave_max_u32(bmax);
-  if (lane == 0) sm.wc[wave] = bmax;
   __syncthreads();
-  bmax = __builtin_amdgcn_readfirstlane(wave_max_u32(lane < kSelWaves ? sm.wc[lane] : 0u));
-  if (bmax > 0x7f800000u) return false;
   // counted from the top: protected keys and padding sit in bin 4095
   uint32_t need = (uint32_t)kept + npad, d1, above;
   find_bin<4>(sm.hist, need, sm, tid, lane, wave, d1, above);
@@ -467,40 +487,52 @@ __device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int 
     const bool edge = sv.edge(r);
     if (nr > 1) {
       sv.load_raw(r, key);
-      if (edge) sv.specials(r, key);
+      if (edge) {
+        sv.specials(r, key);
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j) key[j] -= kmn;
+      }
     }
     const int p0 = sv.seg0(r) + lane;
     uint32_t nhi = 0u;
 #pragma unroll
     for (int j = 0; j < kSelKpt; ++j) {
-      const uint32_t bin = key[j] >> 20;  // specials give 4095
-      nhi += (uint32_t)__popcll(__ballot(edge ? (bin > d1 && key[j] != kPad) : bin > d1));
+      const uint32_t k = key[j];
+      const uint32_t bin = k < kPad ? k >> sh : 4095u;
+      nhi += (uint32_t)__popcll(__ballot(bin > d1 && k != kPad));
       if (bin == d1) {
         const uint32_t slot = atomicAdd(&sm.ncand, 1u);
-        sm.ckey[slot] = key[j];
+        sm.ckey[slot] = k;
         sm.cpos[slot] = p0 + 64 * j;
       }
     }
     if (lane == 0) sm.rw_def[r * kSelWaves + wave] = nhi;
   }
-  // the bin's low 20 bits: 11, then 9, on the LDS copy
-  for (int i = tid; i < 2048; i += kSelThreads) sm.hist[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < (int)c1; i += kSelThreads) atomicAdd(&sm.hist[(sm.ckey[i] >> 9) & 2047u], 1u);
-  __syncthreads();
-  uint32_t da, db;
-  find_bin<2>(sm.hist, need, sm, tid, lane, wave, da, above);
-  need -= above;
-  for (int i = tid; i < 2048; i += kSelThreads) sm.hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < (int)c1; i += kSelThreads) {
-    const uint32_t k = sm.ckey[i];
-    if (((k >> 9) & 2047u) == da) atomicAdd(&sm.hist[k & 511u], 1u);
+  // the bin's low sh bits, at most 11 per pass, on the LDS copy
+  uint32_t pfx = d1;
+  int pfx_sh = sh;
+  while (pfx_sh > 0) {
+    const int nbits = pfx_sh < 11 ? pfx_sh : 11;
+    const int sel_sh = pfx_sh - nbits;
+    const uint32_t mask = (1u << nbits) - 1u;
+    for (int i = tid; i < 2048; i += kSelThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < (int)c1; i += kSelThreads) {
+      const uint32_t v = sm.ckey[i];
+      if ((v >> pfx_sh) == pfx) atomicAdd(&sm.hist[(v >> sel_sh) & mask], 1u);
+    }
+    __syncthreads();
+    uint32_t dsel;
+    find_bin<2>(sm.hist, need, sm, tid, lane, wave, dsel, above);
+    need -= above;
+    pfx = (pfx << nbits) | dsel;
+    pfx_sh = sel_sh;
   }
-  __syncthreads();
-  find_bin<2>(sm.hist, need, sm, tid, lane, wave, db, above);
-  need -= above;
-  const uint32_t thr = (d1 << 20) | (da << 9) | db;
+  const uint32_t thr = pfx;  // rebased
   const uint32_t rem = need;
 
   // add the bin's keys above / equal to thr to the per-(round, wave) counts
@@ -545,7 +577,14 @@ __device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int 
     const bool edge = sv.edge(r);
     if (nr > 1) {
       sv.load_raw(r, key);
-      if (edge) sv.specials(r, key);
+      if (edge) {
+        sv.specials(r, key);
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j) key[j] = key[j] < kPad ? key[j] - kmn : key[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kSelKpt; ++j) key[j] -= kmn;
+      }
     }
     const uint32_t D = sm.rw_def[r * kSelWaves + wave], Tt = sm.rw_tie[r * kSelWaves + wave];
     emit_round(key, edge, thr, rem, D, Tt, sv.seg0(r) + lane, kept, out);
