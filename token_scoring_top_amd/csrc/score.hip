@@ -198,6 +198,121 @@ __device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[D / 16], const __bf16*
 // (j % 4) and column lane % 32.
 __device__ __forceinline__ int c_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
+// Column sums of one 32-key tile over the wave's 64 query rows: logits of
+// both 32-row query tiles on v_mfma_f32_32x32x16_bf16 (queries as rows, this
+// lane's key as the column), then sum over the lane's 32 rows of
+// p = exp2(x c2 - M_row); when MASK, rows whose last visible key (rl, from
+// LDS) is below this lane's key are dropped, and so is a key past `last`.
+// The lane's rows of a tile are 4 runs of 4 consecutive rows, read from LDS
+// as broadcast float4s / int4s.  The two MFMA chains are independent: the second one
+// is interleaved with the first one's exponentials, and four partial sums
+// keep the exp / add dependency chains short.
+template <int D, bool MASK>
+__device__ __forceinline__ float tile_col_sums(const bf16x8 (&qf)[2][D / 16],
+                                               const bf16x8 (&kf)[D / 16], const float* mr,
+                                               const int* rl, float c2, int lane, int key,
+                                               int last) {
+  constexpr int KS = D / 16;
+  f32x16 acc[2] = {{}, {}};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][kk], kf[kk], acc[0], 0, 0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][kk], kf[kk], acc[1], 0, 0, 0);
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  // re-read the normalisers every tile rather than holding 32 of them in
+  // registers across the loop (the opaque offset keeps them from being hoisted)
+  int moff = 4 * (lane >> 5);
+  asm volatile("" : "+v"(moff));
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float Mr[16];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 v = *(const f32x4*)&mr[qt * 32 + 8 * jj + moff];
+      Mr[4 * jj] = v[0];
+      Mr[4 * jj + 1] = v[1];
+      Mr[4 * jj + 2] = v[2];
+      Mr[4 * jj + 3] = v[3];
+    }
+    int Lr[16];
+    if constexpr (MASK) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int4 v = *(const int4*)&rl[qt * 32 + 8 * jj + moff];
+        Lr[4 * jj] = v.x;
+        Lr[4 * jj + 1] = v.y;
+        Lr[4 * jj + 2] = v.z;
+        Lr[4 * jj + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float p = fast_exp2(fmaf(acc[qt][j], c2, -Mr[j]));
+      if constexpr (MASK)
+        ps[j & 3] += key <= Lr[j] ? p : 0.f;
+      else
+        ps[j & 3] += p;
+    }
+  }
+  // MFMA(acc1) k-steps interleaved with the VALU work on acc0
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+  const float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  return (!MASK || key <= last) ? sum : 0.f;
+}
+
+// Row statistics of one 32-key tile for the wave's 64 query rows: logits on
+// v_mfma_f32_32x32x16_bf16 with keys as rows, so lane l holds 16 keys of
+// query row l % 32 of each 32-row tile; the lane's running maximum m and sum
+// s of exp2(x c2 - m) absorb them (keys past the row's limit lim masked when
+// MASK).  As in the column sums, the second MFMA chain is interleaved with
+// the first one's VALU work and partial sums keep dependency chains short.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_row_stats(const bf16x8 (&qf)[2][D / 16],
+                                               const bf16x8 (&kf)[D / 16], float c2, int key0,
+                                               const int (&lim)[2], int lane, float (&m)[2],
+                                               float (&s)[2]) {
+  constexpr int KS = D / 16;
+  f32x16 acc[2] = {{}, {}};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[0][kk], acc[0], 0, 0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[1][kk], acc[1], 0, 0, 0);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    if constexpr (MASK) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (key0 + c_row(j, lane) > lim[qt]) acc[qt][j] = -INFINITY;
+    }
+    float t4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      t4[e] = fmaxf(fmaxf(acc[qt][4 * e], acc[qt][4 * e + 1]),
+                    fmaxf(acc[qt][4 * e + 2], acc[qt][4 * e + 3]));
+    const float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    const float mn = fmaxf(m[qt], tmax * c2);
+    const float mref = fmaxf(mn, -1.0e30f);  // all keys masked so far: stay at zero
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ps[j & 3] += fast_exp2(fmaf(acc[qt][j], c2, -mref));
+    s[qt] = fmaf(s[qt], fast_exp2(m[qt] - mref), (ps[0] + ps[1]) + (ps[2] + ps[3]));
+    m[qt] = mn;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+  }
+}
+
 // Sweep the 32-key tiles [first, end) with stride STEP, software-pipelined:
 // the next tile's loads are issued before the current tile is reduced, so a
 // wave keeps HBM requests in flight while it computes.  Every path issues the
@@ -265,29 +380,12 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
     sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane,
                          [&](const bf16x8 (&kf)[KS], int64_t key0) {
-      const bool full = (int)key0 + 31 <= minlim;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[qt][kk], acc, 0, 0, 0);
-        if (!full) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if ((int)key0 + c_row(j, lane) > lim[qt]) acc[j] = -INFINITY;
-        }
-        float tmax = acc[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, acc[j]);
-        const float mn = fmaxf(m[qt], tmax * a.c2);
-        const float mref = fmaxf(mn, -1.0e30f);  // all keys masked so far: stay at zero
-        float add = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) add += fast_exp2(fmaf(acc[j], a.c2, -mref));
-        s[qt] = fmaf(s[qt], fast_exp2(m[qt] - mref), add);
-        m[qt] = mn;
-      }
+      // fully visible tiles (nearly all) and masked ones get separate
+      // straight-line copies
+      if ((int)key0 + 31 <= minlim)
+        tile_row_stats<D, false>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
+      else
+        tile_row_stats<D, true>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
     });
     // lanes l and l + 32 hold the same rows over different keys
 #pragma unroll
@@ -341,9 +439,14 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     // 4 consecutive rows, the same for every lane of a half-wave, so they are
     // read as broadcast float4s instead of being held in 32 registers
     __shared__ __attribute__((aligned(16))) float mrow[64 * NRG];
+    // last visible key of every row (the whole sequence for padding rows)
+    __shared__ __attribute__((aligned(16))) int rlim[64 * NRG];
     int* done2 = ctl + U;
     const float* rs = rowstat + (int64_t)u * a.Mpad;
-    for (int r = tid; r < a.Mpad; r += TH) mrow[r] = rs[r];
+    for (int r = tid; r < a.Mpad; r += TH) {
+      mrow[r] = rs[r];
+      rlim[r] = row_limit(a, N, r, N - 1);
+    }
     __syncthreads();
     double hs = 0.0, ha = 0.0;
     float* so = s_out + (int64_t)lh * a.T + st.cu[b];
@@ -354,35 +457,16 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane,
                            [&](const bf16x8 (&kf)[KS], int64_t key0) {
         const int key = (int)key0 + (lane & 31);
-        const bool full = (int)key0 + 31 <= minlim;
-        float cv = 0.f;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x16 acc = {};
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][kk], kf[kk], acc, 0, 0, 0);
-          float Mr[16];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 v = *(const f32x4*)&mrow[rg * 64 + qt * 32 + 8 * jj + 4 * (lane >> 5)];
-            Mr[4 * jj] = v[0];
-            Mr[4 * jj + 1] = v[1];
-            Mr[4 * jj + 2] = v[2];
-            Mr[4 * jj + 3] = v[3];
-          }
-          if (full) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) cv += fast_exp2(fmaf(acc[j], a.c2, -Mr[j]));
-          } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const float p = fast_exp2(fmaf(acc[j], a.c2, -Mr[j]));
-              const int r = rg * 64 + qt * 32 + c_row(j, lane);
-              cv += key <= row_limit(a, N, r, last) ? p : 0.f;
-            }
-          }
-        }
+        // fully visible tiles (nearly all) and masked ones get separate
+        // straight-line copies, so the scheduler can overlap the second MFMA
+        // chain with the first chain's exponentials
+        float cv;
+        if ((int)key0 + 31 <= minlim)
+          cv = tile_col_sums<D, false>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                       last);
+        else
+          cv = tile_col_sums<D, true>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                      last);
         cv += __shfl_xor(cv, 32);
         if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
       });
