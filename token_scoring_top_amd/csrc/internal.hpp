@@ -38,10 +38,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- score -----------------------------------------------------------------
-// Keys per work-group chunk: a multiple of this on the MFMA path (grown for
-// long sequences), fixed on the fp32 VALU path.
+// Keys per work-group chunk: a multiple of this on the MFMA path (sized so
+// the grid holds about kScoreGroups work-groups), fixed on the fp32 VALU path.
 constexpr int kScoreChunkMfma = 1024;
 constexpr int kScoreChunkF32 = 256;
+constexpr int64_t kScoreGroups = 256;  // MI355X compute units
 
 struct ScoreGeom {
   int M;       // G * W query rows per KV head
@@ -51,8 +52,9 @@ struct ScoreGeom {
   size_t off_part1, off_rowstat, off_part2, off_ctl, bytes;
 };
 
-// Chunk size the score path uses for these sequence lengths.
-int score_chunk(int B, const int64_t* seqlens, int dtype);
+// Chunk size the score path uses for these sequence lengths and `units`
+// (layers x KV heads) independent score problems.
+int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype);
 
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype);
 
