@@ -6,9 +6,10 @@
 One step = the whole prefill path over one batch of synthetic input already
 resident in HBM: hubkv_score -> hubkv_refine -> hubkv_select -> hubkv_compact
 (every KV head, every layer of the workload).  Prints one JSON line with
-scored+selected tokens per second per head, per-op times measured with HIP
-events on the launch stream, the roofline position of the dominant op, and
-the CPU oracle timed on this host's cores on a bounded sample.
+scored+selected tokens per second per head (K steps timed back to back
+between two synchronisations), per-op times measured with HIP events on the
+launch stream over K further steps, the roofline position of the dominant
+op, and the CPU oracle timed on this host's cores on a bounded sample.
 
 Default workload: the Llama-2-7B-shaped layer (32 MHA heads, d 128, 32768
 tokens, window 64, 10% kept with 4 sink and 64 recent tokens, bf16).
@@ -170,14 +171,21 @@ def main(argv=None):
 
     for _ in range(args.warmup):
         step()
+    # timed region: whole steps back to back, no markers between the ops
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # per-op times: the same number of steps again, with HIP events recorded
+    # on the launch stream between the ops (the markers cost a little time,
+    # so these steps are not the ones `value` comes from)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     names = ["score", "refine", "select", "compact"]
     op_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, n in enumerate(names)}

@@ -5,8 +5,7 @@
 //   K_out[l][g][o_b + j] = K[l][g][cu_b + idx[l][g][o_b + j]]   (same for V)
 // Each thread moves 16-byte pieces of rows; a 256-byte bf16 row (d = 128) is
 // 16 consecutive lanes, so every wave reads and writes whole rows with fully
-// used 64-byte segments.  Several pieces per thread are loaded before any is
-// stored, to keep enough reads in flight.
+// used 64-byte segments.
 #include "internal.hpp"
 
 namespace hubkv {
@@ -25,44 +24,53 @@ __device__ __forceinline__ int seq_of_row(const SeqTable& st, int64_t row) {
   return lo;
 }
 
+// Rows of 1 << LOGP 16-byte pieces: a group of 1 << LOGP consecutive lanes
+// moves one row, so a wave reads and writes whole rows.  Each thread first
+// loads the kept positions of its kUnroll rows, then their K and V pieces
+// (2 kUnroll 16-byte loads in flight), then stores them (non-temporal: the
+// packed cache is not read again here).
+template <int LOGP>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     const u32x4* __restrict__ k_in, const u32x4* __restrict__ v_in,
-    const int32_t* __restrict__ idx, SeqTable st, int64_t T, int64_t Ktot, int pieces,
+    const int32_t* __restrict__ idx, SeqTable st, int64_t T, int64_t Ktot,
     u32x4* __restrict__ k_out, u32x4* __restrict__ v_out) {
+  constexpr int P = 1 << LOGP;
+  constexpr int RPI = kCompactThreads / P;  // rows per unrolled step
+  constexpr int RB = RPI * kUnroll;          // rows per block iteration
   const int lh = blockIdx.y;
-  const int64_t total = Ktot * pieces;
-  const int64_t stride = (int64_t)gridDim.x * kCompactThreads;
+  const int pc = threadIdx.x & (P - 1);
+  const int rsub = threadIdx.x >> LOGP;
   const int32_t* ih = idx + (int64_t)lh * Ktot;
-  const u32x4* kin = k_in + (int64_t)lh * T * pieces;
-  const u32x4* vin = v_in + (int64_t)lh * T * pieces;
-  u32x4* ko = k_out + (int64_t)lh * Ktot * pieces;
-  u32x4* vo = v_out + (int64_t)lh * Ktot * pieces;
-  for (int64_t f0 = (int64_t)blockIdx.x * kCompactThreads + threadIdx.x; f0 < total;
-       f0 += stride * kUnroll) {
-    u32x4 kv[kUnroll], vv[kUnroll];
-    int64_t dst[kUnroll];
+  const u32x4* kin = k_in + (int64_t)lh * T * P;
+  const u32x4* vin = v_in + (int64_t)lh * T * P;
+  u32x4* ko = k_out + (int64_t)lh * Ktot * P;
+  u32x4* vo = v_out + (int64_t)lh * Ktot * P;
+  for (int64_t row0 = (int64_t)blockIdx.x * RB; row0 < Ktot; row0 += (int64_t)gridDim.x * RB) {
+    int64_t src[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t f = f0 + u * stride;
-      dst[u] = -1;
-      if (f < total) {
-        const int64_t row = f / pieces;
-        const int pc = (int)(f - row * pieces);
-        const int b = seq_of_row(st, row);
+      const int64_t row = row0 + u * RPI + rsub;
+      src[u] = -1;
+      if (row < Ktot) {
+        const int b = st.B == 1 ? 0 : seq_of_row(st, row);
         const int32_t p = ih[row];
-        if (p >= 0 && p < st.N[b]) {
-          const int64_t src = (st.cu[b] + p) * pieces + pc;
-          kv[u] = kin[src];
-          vv[u] = vin[src];
-          dst[u] = f;
-        }
+        if (p >= 0 && p < st.N[b]) src[u] = (st.cu[b] + p) * P + pc;
+      }
+    }
+    u32x4 kv[kUnroll], vv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (src[u] >= 0) {
+        kv[u] = kin[src[u]];
+        vv[u] = vin[src[u]];
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (dst[u] >= 0) {
-        ko[dst[u]] = kv[u];
-        vo[dst[u]] = vv[u];
+      if (src[u] >= 0) {
+        const int64_t dst = (row0 + u * RPI + rsub) * P + pc;
+        __builtin_nontemporal_store(kv[u], &ko[dst]);
+        __builtin_nontemporal_store(vv[u], &vo[dst]);
       }
     }
   }
@@ -79,13 +87,23 @@ hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, co
     K += st.kept[b];
   }
   if (K == 0) return hipSuccess;
-  const int pieces = d * elem_bytes / 16;
-  const int64_t total = K * pieces;
-  int64_t blocks = (total + (int64_t)kCompactThreads * kUnroll - 1) / ((int64_t)kCompactThreads * kUnroll);
+  const int pieces = d * elem_bytes / 16;  // 8, 16 or 32
+  const int logp = pieces == 8 ? 3 : (pieces == 16 ? 4 : 5);
+  const int64_t rb = (int64_t)(kCompactThreads / pieces) * kUnroll;
+  int64_t blocks = (K + rb - 1) / rb;
   if (blocks > 65535) blocks = 65535;
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks, L * Hkv), dim3(kCompactThreads), 0,
-                     stream, (const u32x4*)k_in, (const u32x4*)v_in, idx, st, T, K, pieces,
-                     (u32x4*)k_out, (u32x4*)v_out);
+  const dim3 grid((unsigned)blocks, L * Hkv), block(kCompactThreads);
+  const u32x4* ki = (const u32x4*)k_in;
+  const u32x4* vi = (const u32x4*)v_in;
+  if (logp == 3)
+    hipLaunchKernelGGL(compact_kernel<3>, grid, block, 0, stream, ki, vi, idx, st, T, K,
+                       (u32x4*)k_out, (u32x4*)v_out);
+  else if (logp == 4)
+    hipLaunchKernelGGL(compact_kernel<4>, grid, block, 0, stream, ki, vi, idx, st, T, K,
+                       (u32x4*)k_out, (u32x4*)v_out);
+  else
+    hipLaunchKernelGGL(compact_kernel<5>, grid, block, 0, stream, ki, vi, idx, st, T, K,
+                       (u32x4*)k_out, (u32x4*)v_out);
   return hipGetLastError();
 }
 

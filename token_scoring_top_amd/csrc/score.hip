@@ -118,7 +118,11 @@ __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const
 // writer's stores completed (s_waitcnt vmcnt(0)), so no cache write-back or
 // invalidation is needed.
 // --------------------------------------------------------------------------
-constexpr int kSub = 1024;  // keys per column-sum round in pass 2
+// Keys per column-sum round in pass 2: 32 KiB of LDS partial sums whatever
+// the number of 64-row groups, so a 4096-key chunk with one row group is a
+// single round (K keeps streaming without a barrier in between).
+template <int NRG>
+constexpr int sub_keys() { return 8192 / NRG; }
 
 __device__ __forceinline__ void st_agent(float2* p, float2 v) {
   __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v),
@@ -444,6 +448,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
     // key0 + l % 32 and 16 rows of each query tile, so a column sum is a
     // lane-local sum plus one exchange between the two half-waves.
+    constexpr int kSub = sub_keys<NRG>();
     __shared__ float cs[NRG][kSub];
     __shared__ double2 hred[WAVES];
     // row normalisers in LDS: a lane's 16 rows of a query tile are 4 runs of
