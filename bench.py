@@ -202,7 +202,7 @@ def main(argv=None):
     rsc_bytes = nb["refine"] + nb["select"] + nb["compact"]
     rsc_ms = op_ms["refine"] + op_ms["select"] + op_ms["compact"]
     mfma_util = score_flops(w) / (op_ms["score"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12)
-    kernels = {"score": "fill_zero_i32 + score_pass_mfma<1> (row stats) + score_pass_mfma<2> (column sums)" if elem == 2 else
+    kernels = {"score": "score_pass_mfma<1> (row partials) + score_pass_mfma<2> (fold, column sums)" if elem == 2 else
                "score_stats_f32 + score_combine + score_probs_f32 + stats_final",
                "refine": "refine_kernel", "select": "select_kernel",
                "compact": "compact_kernel"}

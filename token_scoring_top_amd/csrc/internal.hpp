@@ -49,7 +49,7 @@ struct ScoreGeom {
   int Mpad;    // rows rounded up to 64
   int chunk;   // keys per work-group task
   int nchunk;  // chunks over all sequences of one (layer, KV head)
-  size_t off_part1, off_rowstat, off_part2, off_ctl, bytes;
+  size_t off_part1, off_rowstat, off_part2, off_ctl, bytes;  // rowstat: fp32 path only
 };
 
 // Chunk size the score path uses for these sequence lengths and `units`

@@ -424,7 +424,6 @@ __device__ __forceinline__ bool select_fast(const SelView& sv, SelSmem& sm, int 
                                             uint32_t npad, int kept, int32_t* __restrict__ out,
                                             int tid, int lane, int wave) {
   if (nr > kFastRounds) return false;
-  const int N = sv.N, a = sv.a, c = sv.c;
   uint32_t key[kSelKpt];
   // sweep 0: range of the candidates' raw bits; bits above +inf's
   // (0x7f800000) belong to a NaN or a negative value

@@ -88,7 +88,7 @@ ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int 
   g.off_rowstat = align256(LH * g.nchunk * g.Mpad * sizeof(float2));
   g.off_part2 = g.off_rowstat + align256(U * g.Mpad * sizeof(float));
   g.off_ctl = g.off_part2 + align256(LH * g.nchunk * 2 * sizeof(double));
-  g.bytes = g.off_ctl + align256(2 * U * sizeof(int));
+  g.bytes = g.off_ctl + align256(U * sizeof(int));
   return g;
 }
 
@@ -104,19 +104,21 @@ __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const
 
 // --------------------------------------------------------------------------
 // bf16 MFMA path: two launches over (chunk, layer-head) grids.
-//   pass 1: each work-group reduces its chunk to per-row partials (m, l) and
-//           counts itself in; the work-group that counts last for its unit
-//           (layer-head, sequence) folds all the unit's partials into the row
-//           normalisers M = m + log2(l).
-//   pass 2: each work-group recomputes its chunk's logits, sums p = exp2(x - M)
-//           down every key column, writes s and its chunk's {sum s, sum s ln s};
-//           the last one of a unit adds the unit's chunks up in chunk order.
+//   pass 1: each work-group reduces its chunk to per-row partials (m, l); the
+//           unit's (layer-head, sequence) first chunk clears the unit's
+//           pass-2 counter.
+//   pass 2: each work-group first folds its unit's partials into the row
+//           normalisers M = m + log2(l) (every work-group of a unit computes
+//           the same values), then recomputes its chunk's logits, sums
+//           p = exp2(x - M) down every key column, writes s and its chunk's
+//           {sum s, sum s ln s}, and counts itself in; the last one of a unit
+//           to count in adds the unit's chunks up in chunk order.
 // Nobody waits for anybody (the last one to arrive does the fold), so no
-// schedule can deadlock.  The counters live in the workspace and are zeroed
-// by a fill kernel first.  Partials read by the folding work-group go through
-// agent-scope coherent accesses, and a counter is bumped only after the
-// writer's stores completed (s_waitcnt vmcnt(0)), so no cache write-back or
-// invalidation is needed.
+// schedule can deadlock, and no separate clearing launch is needed.  The
+// chunk statistics read by the folding work-group go through agent-scope
+// coherent accesses, and a counter is bumped only after the writer's stores
+// completed (s_waitcnt vmcnt(0)), so no cache write-back or invalidation is
+// needed.
 // --------------------------------------------------------------------------
 // Keys per column-sum round in pass 2: 32 KiB of LDS partial sums whatever
 // the number of 64-row groups, so a 4096-key chunk with one row group is a
@@ -356,13 +358,12 @@ __device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t first, int
 template <int D, int NRG, int NKG, int PHASE>
 __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, SeqTable st, ScoreArgs a,
-    int* __restrict__ ctl, float2* __restrict__ part1, float* __restrict__ rowstat,
-    double2* __restrict__ part2, float* __restrict__ s_out, double* __restrict__ stats) {
+    int* __restrict__ ctl, float2* __restrict__ part1, double2* __restrict__ part2,
+    float* __restrict__ s_out, double* __restrict__ stats) {
   constexpr int TH = 64 * NRG * NKG;
   constexpr int WAVES = NRG * NKG;
   constexpr int STEP = 32 * NKG;
   constexpr int KS = D / 16;
-  const int U = a.L * a.Hkv * st.B;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int rg = wave % NRG, kg = wave / NRG;
@@ -385,8 +386,6 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     // row 64 rg + 32 qt + l % 32 and 16 of the tile's keys, so the running
     // row maximum and sum are lane-local.
     __shared__ float2 red[NKG][64 * NRG];
-    __shared__ int sh_last;
-    int* arrive = ctl;
     const int last = (int)key_end - 1;
     const int minlim = wave_min_limit(a, N, rg, lane, last);
     int lim[2];
@@ -413,36 +412,16 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       if (lane < 32) red[kg][rg * 64 + qt * 32 + lane] = make_float2(fmaxf(m[qt], kMinit), s[qt]);
     }
     __syncthreads();
-    // wave 0 publishes the chunk's partials, then counts the chunk in
+    // wave 0 publishes the chunk's partials (read by pass 2, after this
+    // launch); the unit's first chunk also clears the unit's pass-2 counter
     if (wave == 0) {
       for (int rl = lane; rl < a.Mpad; rl += 64) {
         float mm = red[0][rl].x, ss = red[0][rl].y;
 #pragma unroll
         for (int q = 1; q < NKG; ++q) merge_ml(mm, ss, red[q][rl].x, red[q][rl].y);
-        st_agent(&part1[((int64_t)lh * a.nchunk + chunk_g) * a.Mpad + rl], make_float2(mm, ss));
+        part1[((int64_t)lh * a.nchunk + chunk_g) * a.Mpad + rl] = make_float2(mm, ss);
       }
-      wait_stores();
-      if (lane == 0) sh_last = (bump_agent(&arrive[u]) == nch - 1);
-    }
-    __syncthreads();
-    if (sh_last) {
-      // the unit's last chunk: fold every chunk's partials into M = m + log2(l)
-      const float2* pp = part1 + ((int64_t)lh * a.nchunk + st.tile_off[b]) * a.Mpad;
-      for (int r = tid; r < a.Mpad; r += TH) {
-        float mm = kMinit, ss = 0.f;
-        for (int cc = 0; cc < nch; cc += 8) {
-          float2 pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pv[e] = cc + e < nch ? ld_agent(&pp[(int64_t)(cc + e) * a.Mpad + r])
-                                 : make_float2(kMinit, 0.f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (pv[e].y > 0.f) merge_ml(mm, ss, pv[e].x, pv[e].y);
-        }
-        rowstat[(int64_t)u * a.Mpad + r] =
-            (r < a.M && ss > 0.f) ? mm + __builtin_amdgcn_logf(ss) : INFINITY;
-      }
+      if (c == 0 && lane == 0) ctl[u] = 0;
     }
   } else {
     // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
@@ -457,10 +436,23 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     __shared__ __attribute__((aligned(16))) float mrow[64 * NRG];
     // last visible key of every row (the whole sequence for padding rows)
     __shared__ __attribute__((aligned(16))) int rlim[64 * NRG];
-    int* done2 = ctl + U;
-    const float* rs = rowstat + (int64_t)u * a.Mpad;
+    int* done2 = ctl;
+    // fold every chunk's pass-1 partials of this unit into the row
+    // normalisers M = m + log2(l), in chunk order (every work-group of the
+    // unit computes the same values)
+    const float2* pp = part1 + ((int64_t)lh * a.nchunk + st.tile_off[b]) * a.Mpad;
     for (int r = tid; r < a.Mpad; r += TH) {
-      mrow[r] = rs[r];
+      float mm = kMinit, ss = 0.f;
+      for (int cc = 0; cc < nch; cc += 8) {
+        float2 pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pv[e] = cc + e < nch ? pp[(int64_t)(cc + e) * a.Mpad + r] : make_float2(kMinit, 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (pv[e].y > 0.f) merge_ml(mm, ss, pv[e].x, pv[e].y);
+      }
+      mrow[r] = (r < a.M && ss > 0.f) ? mm + __builtin_amdgcn_logf(ss) : INFINITY;
       rlim[r] = row_limit(a, N, r, N - 1);
     }
     __syncthreads();
@@ -530,10 +522,6 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_i32(int* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
 
 // --------------------------------------------------------------------------
 // fp32 VALU path: one key per thread, query rows staged through LDS in
@@ -728,21 +716,16 @@ template <int D, int NRG, int NKG>
 hipError_t run_mfma(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
                     char* ws, const ScoreGeom& geo, float* s, double* stats,
                     hipStream_t stream) {
-  const int U = a.L * a.Hkv * st.B;
   int* ctl = (int*)(ws + geo.off_ctl);
-  hipLaunchKernelGGL(fill_zero_i32, dim3((2 * U + 255) / 256), dim3(256), 0, stream, ctl, 2 * U);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid(a.nchunk, a.L * a.Hkv), block(64 * NRG * NKG);
   float2* part1 = (float2*)(ws + geo.off_part1);
-  float* rowstat = (float*)(ws + geo.off_rowstat);
   double2* part2 = (double2*)(ws + geo.off_part2);
   hipLaunchKernelGGL((score_pass_mfma<D, NRG, NKG, 1>), grid, block, 0, stream, (const __bf16*)q,
-                     (const __bf16*)k, st, a, ctl, part1, rowstat, part2, s, stats);
-  e = hipGetLastError();
+                     (const __bf16*)k, st, a, ctl, part1, part2, s, stats);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((score_pass_mfma<D, NRG, NKG, 2>), grid, block, 0, stream, (const __bf16*)q,
-                     (const __bf16*)k, st, a, ctl, part1, rowstat, part2, s, stats);
+                     (const __bf16*)k, st, a, ctl, part1, part2, s, stats);
   return hipGetLastError();
 }
 
