@@ -42,7 +42,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // the grid holds about kScoreGroups work-groups), fixed on the fp32 VALU path.
 constexpr int kScoreChunkMfma = 1024;
 constexpr int kScoreChunkF32 = 256;
-constexpr int64_t kScoreGroups = 256;  // MI355X compute units
+constexpr int64_t kScoreGroups = 256;     // MI355X compute units
+constexpr int64_t kScoreStartKeys = 2048;  // per-work-group start-up, in keys streamed
 
 struct ScoreGeom {
   int M;       // G * W query rows per KV head

@@ -54,24 +54,30 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype) {
   if (dtype != 1) return kScoreChunkF32;
-  // About one work-group per compute unit over the whole grid: each wave then
-  // streams a long run of K tiles and pays the per-work-group start-up (Q
-  // fragments, partial publishing) once.  On the Llama-2-7B-shaped layer this
-  // measured 102 us for the score op against 131 us with 1024-key chunks and
-  // 151 us with one work-group per two compute units.
-  int64_t T = 0, mx = 0;
-  for (int b = 0; b < B; ++b) {
-    const int64_t n = seqlens[b] > 0 ? seqlens[b] : 0;
-    T += n;
-    mx = n > mx ? n : mx;
-  }
+  // Chunks in multiples of 1024 keys, chosen to minimise the makespan
+  // (rounds of kScoreGroups work-groups) x (chunk + a fixed start-up cost of
+  // kScoreStartKeys keys): long runs of K tiles per wave, about one
+  // work-group per compute unit, no straggling second round.  On the
+  // Llama-2-7B-shaped layer 4096-key chunks (256 work-groups) measured
+  // 102 us for the score op against 131 us with 1024-key chunks.
+  int64_t mx = 0;
+  for (int b = 0; b < B; ++b) mx = seqlens[b] > mx ? seqlens[b] : mx;
   if (units < 1) units = 1;
-  int64_t c = (T * units + kScoreGroups - 1) / kScoreGroups;
-  const int64_t cap = (mx + kScoreChunkMfma - 1) / kScoreChunkMfma * kScoreChunkMfma;
-  c = (c + kScoreChunkMfma - 1) / kScoreChunkMfma * kScoreChunkMfma;
-  if (c > cap) c = cap;
-  if (c > ((int64_t)1 << 30)) c = (int64_t)1 << 30;
-  return (int)(c < kScoreChunkMfma ? kScoreChunkMfma : c);
+  const int64_t top = (mx + kScoreChunkMfma - 1) / kScoreChunkMfma;
+  int64_t best_c = kScoreChunkMfma, best_cost = INT64_MAX;
+  for (int64_t m = 1; m <= top && m <= ((int64_t)1 << 20); ++m) {
+    const int64_t c = m * kScoreChunkMfma;
+    int64_t groups = 0;
+    for (int b = 0; b < B; ++b) groups += (seqlens[b] + c - 1) / c;
+    groups *= units;
+    const int64_t rounds = (groups + kScoreGroups - 1) / kScoreGroups;
+    const int64_t cost = rounds * (c + kScoreStartKeys);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_c = c;
+    }
+  }
+  return (int)best_c;
 }
 
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype) {
@@ -120,11 +126,24 @@ __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const
 // completed (s_waitcnt vmcnt(0)), so no cache write-back or invalidation is
 // needed.
 // --------------------------------------------------------------------------
-// Keys per column-sum round in pass 2: 32 KiB of LDS partial sums whatever
-// the number of 64-row groups, so a 4096-key chunk with one row group is a
-// single round (K keeps streaming without a barrier in between).
-template <int NRG>
-constexpr int sub_keys() { return 8192 / NRG; }
+// Shared K staging (row groups NRG >= 2): each stage holds 32 keys per row
+// group, rows padded to 2 D + 16 bytes so the lanes' 16-byte fragment reads
+// fall in distinct LDS banks.
+template <int D, int NRG>
+constexpr int stage_bytes() { return NRG > 1 ? 32 * NRG * (2 * D + 16) : 16; }
+
+// Keys per column-sum round in pass 2.  One row group: 32 KiB of LDS partial
+// sums, so a 4096-key chunk is a single round (K keeps streaming without a
+// barrier in between).  Several row groups: about 20 KiB of LDS per row group
+// in total (so small work-groups still share a compute unit), in whole stages.
+template <int D, int NRG>
+constexpr int sub_keys() {
+  if (NRG == 1) return 8192;
+  constexpr int sk = 32 * NRG;
+  constexpr int budget = (20 * 1024 * NRG < 150 * 1024 ? 20 * 1024 * NRG : 150 * 1024);
+  constexpr int n = (budget - stage_bytes<D, NRG>() - 4096) / (4 * NRG) / sk;
+  return sk * (n > 1 ? n : 1);
+}
 
 __device__ __forceinline__ void st_agent(float2* p, float2 v) {
   __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v),
@@ -355,6 +374,57 @@ __device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t first, int
   }
 }
 
+// Sweep [first, end) with the K tiles shared by the work-group's NRG row
+// groups (one wave each): per stage of 32 NRG keys every wave loads one 32-key
+// tile from global memory (whole 256-byte rows per load instruction) into
+// registers, the stage is written to LDS, and every wave then reduces all of
+// the stage's tiles for its own 64 query rows, reading its MFMA fragments from
+// LDS.  The next stage's global loads are in flight during that compute.
+// Each K byte is read from memory once per work-group instead of once per
+// row group.  Past-the-end rows load the last valid key and are masked by the
+// callers.  Called by every thread of the work-group.
+template <int D, int NRG, typename F>
+__device__ __forceinline__ void sweep_stages(const __bf16* Kh, int64_t first, int64_t end,
+                                             char* kst, int lane, int wave, F&& body) {
+  constexpr int ROWB = 2 * D + 16;
+  constexpr int PPR = 2 * D / 16;    // 16-byte pieces per key row
+  constexpr int PPL = 32 * PPR / 64;  // pieces per lane for one 32-key tile
+  constexpr int RPI = 64 / PPR;       // key rows per load instruction
+  constexpr int SK = 32 * NRG;
+  const int nst = __builtin_amdgcn_readfirstlane(
+      first < end ? (int)((end - first + SK - 1) / SK) : 0);
+  if (nst == 0) return;
+  const int prow = lane / PPR, pcol = lane % PPR;
+  u32x4 stg[PPL];
+  auto gload = [&](int64_t s0) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      int64_t key = s0 + 32 * wave + prow + RPI * i;
+      key = key < end ? key : end - 1;
+      stg[i] = *(const u32x4*)(Kh + key * D + pcol * 8);
+    }
+  };
+  gload(first);
+  for (int si = 0; si < nst; ++si) {
+    const int64_t s0 = first + (int64_t)si * SK;
+    __syncthreads();  // the previous stage's readers are done
+#pragma unroll
+    for (int i = 0; i < PPL; ++i)
+      *(u32x4*)(kst + (32 * wave + prow + RPI * i) * ROWB + pcol * 16) = stg[i];
+    __syncthreads();
+    if (si + 1 < nst) gload(s0 + SK);
+    for (int t = 0; t < NRG; ++t) {
+      const int64_t key0 = s0 + 32 * t;
+      if (key0 >= end) break;
+      bf16x8 kf[D / 16];
+      const char* base = kst + (32 * t + (lane & 31)) * ROWB + 16 * (lane >> 5);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const bf16x8*)(base + 32 * kk);
+      body(kf, key0);
+    }
+  }
+}
+
 template <int D, int NRG, int NKG, int PHASE>
 __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, SeqTable st, ScoreArgs a,
@@ -378,6 +448,11 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
   const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
 
+  // several row groups share each K tile through LDS (see sweep_stages)
+  constexpr bool kShared = NRG > 1;
+  static_assert(!kShared || NKG == 1, "shared K staging expects one wave per row group");
+  __shared__ __attribute__((aligned(16))) char kst[stage_bytes<D, NRG>()];
+
   bf16x8 qf[2][KS];
   load_q_frags<D>(qf, Q, a, st, l, g, b, rg, lane);
 
@@ -392,15 +467,16 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) lim[qt] = row_limit(a, N, rg * 64 + qt * 32 + (lane & 31), last);
     float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
-    sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane,
-                         [&](const bf16x8 (&kf)[KS], int64_t key0) {
+    auto body1 = [&](const bf16x8 (&kf)[KS], int64_t key0) {
       // fully visible tiles (nearly all) and masked ones get separate
       // straight-line copies
       if ((int)key0 + 31 <= minlim)
         tile_row_stats<D, false>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
       else
         tile_row_stats<D, true>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
-    });
+    };
+    if constexpr (kShared) sweep_stages<D, NRG>(Kh, key_begin, key_end, kst, lane, wave, body1);
+    else sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane, body1);
     // lanes l and l + 32 hold the same rows over different keys
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -427,7 +503,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
     // key0 + l % 32 and 16 rows of each query tile, so a column sum is a
     // lane-local sum plus one exchange between the two half-waves.
-    constexpr int kSub = sub_keys<NRG>();
+    constexpr int kSub = sub_keys<D, NRG>();
     __shared__ float cs[NRG][kSub];
     __shared__ double2 hred[WAVES];
     // row normalisers in LDS: a lane's 16 rows of a query tile are 4 runs of
@@ -462,8 +538,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       const int64_t sub1 = sub0 + kSub < key_end ? sub0 + kSub : key_end;
       const int last = (int)sub1 - 1;
       const int minlim = wave_min_limit(a, N, rg, lane, last);
-      sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane,
-                           [&](const bf16x8 (&kf)[KS], int64_t key0) {
+      auto body2 = [&](const bf16x8 (&kf)[KS], int64_t key0) {
         const int key = (int)key0 + (lane & 31);
         // fully visible tiles (nearly all) and masked ones get separate
         // straight-line copies, so the scheduler can overlap the second MFMA
@@ -477,7 +552,9 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
                                       last);
         cv += __shfl_xor(cv, 32);
         if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
-      });
+      };
+      if constexpr (kShared) sweep_stages<D, NRG>(Kh, sub0, sub1, kst, lane, wave, body2);
+      else sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane, body2);
       __syncthreads();
       for (int i = tid; i < sub1 - sub0; i += TH) {
         float v = cs[0][i];
@@ -735,7 +812,7 @@ hipError_t dispatch_mfma(const void* q, const void* k, const SeqTable& st, const
                          hipStream_t stream) {
   switch (a.Mpad / 64) {
     case 1: return run_mfma<D, 1, 4>(q, k, st, a, ws, geo, s, stats, stream);
-    case 2: return run_mfma<D, 2, 2>(q, k, st, a, ws, geo, s, stats, stream);
+    case 2: return run_mfma<D, 2, 1>(q, k, st, a, ws, geo, s, stats, stream);
     case 3: return run_mfma<D, 3, 1>(q, k, st, a, ws, geo, s, stats, stream);
     case 4: return run_mfma<D, 4, 1>(q, k, st, a, ws, geo, s, stats, stream);
     case 5: return run_mfma<D, 5, 1>(q, k, st, a, ws, geo, s, stats, stream);
