@@ -93,10 +93,145 @@ def score_flops(w):
     return 2.0 * w.L * w.Hq * w.W * w.T * w.d
 
 
+def h2o_step_bytes(w, elem):
+    """Algorithmic HBM bytes of one h2o_step launch: every retained K row read,
+    acc read and written, pos read, the query, the new K/V rows read, and one
+    slot's K/V/acc/pos written per (sequence, KV head)."""
+    B, Hkv, Hq, d, C = w.B, w.Hkv, w.Hq, w.d, w.C
+    return (B * Hkv * C * (d * elem + 4 + 4 + 4) + B * Hq * d * elem
+            + B * Hkv * (2 * d * elem) + B * Hkv * (2 * d * elem + 8))
+
+
+def bench_decode(args, w):
+    """Streaming H2O decode: the prompt is streamed through h2o_step to build
+    the cache state (untimed), then `steps` decode steps are timed."""
+    import numpy as np
+    import torch
+
+    import token_scoring_top_amd as hk
+
+    steps = 512 if args.steps is None else args.steps
+    B, Hq, Hkv, d, C = w.B, w.Hq, w.Hkv, w.d, w.C
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elem = 2 if w.dtype == "bf16" else 4
+    dev = "cuda"
+    Kc = torch.zeros((B, Hkv, C, d), dtype=dt, device=dev)
+    Vc = torch.zeros_like(Kc)
+    acc = torch.zeros((B, Hkv, C), dtype=torch.float32, device=dev)
+    pos = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
+    ev = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * w.wid)
+    stream = torch.cuda.current_stream()
+    blk = 256
+
+    def inputs(n):
+        # synthetic per-step q, k, v ~ N(0, 1), rounded to the element type
+        q = torch.randn((n, B, Hq, d), generator=gen, device=dev).to(dt)
+        k = torch.randn((n, B, Hkv, d), generator=gen, device=dev).to(dt)
+        v = torch.randn((n, B, Hkv, d), generator=gen, device=dev).to(dt)
+        return q, k, v
+
+    def run(t0, n, evs=None):
+        t = t0
+        while t < t0 + n:
+            m = min(blk, t0 + n - t)
+            q, k, v = inputs(m)
+            for i in range(m):
+                if evs is not None:
+                    evs[t - t0][0].record(stream)
+                hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t, w.scale, w.n_sink, w.recent,
+                            bool(w.include_self), evicted=ev, stream=stream)
+                if evs is not None:
+                    evs[t - t0][1].record(stream)
+                t += 1
+        return t
+
+    # the prompt, streamed token by token (builds the retained cache)
+    t = run(0, w.prompt)
+    t = run(t, args.warmup)
+    # timed decode steps; inputs are drawn before the timed region
+    q, k, v = inputs(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
+                    bool(w.include_self), evicted=ev, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    t += steps
+    ms_step = (t1 - t0) * 1e3 / steps
+    # per-launch kernel time from HIP events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    q, k, v = inputs(steps)
+    for i in range(steps):
+        evs[i][0].record(stream)
+        hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
+                    bool(w.include_self), evicted=ev, stream=stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t += steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = h2o_step_bytes(w, elem)
+    ach = nbytes / (k_ms / 1e3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = min(16, _cores())
+        oracle.set_threads(nthreads)
+        used = oracle.get_threads()
+        # bounded sample: decode steps of the oracle from a copy of the GPU state
+        def f32(x):
+            return np.ascontiguousarray(x.float().cpu().numpy())
+        state = {"K": f32(Kc), "V": f32(Vc), "acc": acc.cpu().numpy().copy(),
+                 "pos": pos.cpu().numpy().copy()}
+        qs, ks, vs = (f32(x) for x in inputs(64))
+        reps, tc0 = 0, time.perf_counter()
+        while reps < 64:
+            oracle.h2o_step(state, qs[reps], ks[reps], vs[reps], t + reps, w.scale, w.n_sink,
+                            w.recent, w.include_self)
+            reps += 1
+            if time.perf_counter() - tc0 >= args.cpu_budget_s:
+                break
+        tc = (time.perf_counter() - tc0) / reps
+        cpu = {"value": C / tc, "unit": "retained-cache tokens/s/head", "cores": used,
+               "kind": "oracle",
+               "sample": f"{reps} decode step(s) of the full batch ({B} x {Hkv} heads x {C} "
+                         f"slots) from a copy of the GPU state, {tc:.3f} s each"}
+
+    out = {
+        "metric": "retained-cache tokens scored per second per head (H2O decode)",
+        "value": C / (ms_step / 1e3),
+        "unit": "tokens/s/head",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "heavy": w.heavy,
+                   "recent": w.recent, "prompt_steps_untimed": w.prompt,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": "h2o_step",
+                     "kernels": "h2o_step_kernel", "algorithmic_bytes": nbytes},
+        "kernel_ms": k_ms,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 512 decode steps for the decode workload)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,8 +258,10 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     w = S.workload(args.workload)
-    if not isinstance(w, S.PrefillWorkload):
-        raise SystemExit("bench.py times the prefill path; pick a prefill workload")
+    if isinstance(w, S.DecodeWorkload):
+        return bench_decode(args, w)
+    if args.steps is None:
+        args.steps = 20
     nthreads = min(16, _cores())
     Q, K, V = S.prefill_inputs(w, threads=nthreads)
     elem = 2 if w.dtype == "bf16" else 4

@@ -20,7 +20,7 @@ namespace hubkv {
 
 namespace {
 
-constexpr int kH2OThreads = 256;
+constexpr int kH2OThreads = 512;
 constexpr int kMaxG = 16;
 constexpr float kLog2eH = 1.4426950408889634f;
 
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   constexpr int WAVES = kH2OThreads / 64;
   extern __shared__ float lg[];  // [G][C] logits in log2 units
   __shared__ float qs[kMaxG][D];
-  __shared__ float red[WAVES][kMaxG];
+  __shared__ float red[WAVES][kMaxG], red2[WAVES][kMaxG];
   __shared__ float Mh[kMaxG], iLh[kMaxG], selfx[kMaxG];
   __shared__ unsigned long long cand_key[WAVES];
   __shared__ int cand_slot[WAVES], empty_w[WAVES];
@@ -73,27 +73,52 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   const int32_t* P = pos + (int64_t)u * C;
   float* A = acc + (int64_t)u * C;
   const int piece = lane % LPR, rsub = lane / LPR;
-  for (int j0 = wave * RPW; j0 < C; j0 += WAVES * RPW) {
-    const int j = j0 + rsub;
-    float kv[EPL];
-    const bool have = j < C;
-    if (have) {
-      const u32x4 raw = *(const u32x4*)(Kc + (int64_t)j * D + piece * EPL);
-      const T* e = (const T*)&raw;
+  float om[kMaxG], os[kMaxG];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    om[h] = -INFINITY;
+    os[h] = 0.f;
+  }
+  // kUnroll row groups per wave are loaded before any is reduced, so each
+  // wave keeps kUnroll 16-byte loads (and their positions) in flight
+  constexpr int kUnroll = 8;
+  for (int j0 = wave * RPW; j0 < C; j0 += WAVES * RPW * kUnroll) {
+    u32x4 raw[kUnroll];
+    int32_t pj[kUnroll];
+#pragma unroll
+    for (int uu = 0; uu < kUnroll; ++uu) {
+      const int j = j0 + uu * WAVES * RPW + rsub;
+      const int jc = j < C ? j : C - 1;  // past-the-end rows read the last slot, never stored
+      raw[uu] = *(const u32x4*)(Kc + (int64_t)jc * D + piece * EPL);
+      pj[uu] = P[jc];
+    }
+#pragma unroll
+    for (int uu = 0; uu < kUnroll; ++uu) {
+      const int j = j0 + uu * WAVES * RPW + rsub;
+      const T* e = (const T*)&raw[uu];
+      float kv[EPL];
 #pragma unroll
       for (int x = 0; x < EPL; ++x) kv[x] = to_f<T>(e[x]);
-    } else {
+      const bool occ = pj[uu] >= 0;
 #pragma unroll
-      for (int x = 0; x < EPL; ++x) kv[x] = 0.f;
-    }
-    const bool occ = have && P[j] >= 0;
-    for (int h = 0; h < G; ++h) {
-      float d = 0.f;
+      for (int h = 0; h < kMaxG; ++h) {
+        if (h >= G) break;
+        float d = 0.f;
 #pragma unroll
-      for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
+        for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
 #pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
-      if (piece == 0 && have) lg[h * C + j] = occ ? d * c2 : -INFINITY;
+        for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+        const float x2 = occ ? d * c2 : -INFINITY;
+        if (piece == 0 && j < C) {
+          lg[h * C + j] = x2;
+          // running softmax statistics of this lane's slots
+          if (x2 > -INFINITY) {
+            const float mn = fmaxf(om[h], x2);
+            os[h] = os[h] * __builtin_amdgcn_exp2f(om[h] - mn) + __builtin_amdgcn_exp2f(x2 - mn);
+            om[h] = mn;
+          }
+        }
+      }
     }
   }
   if (tid < G) {
@@ -108,36 +133,36 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   }
   __syncthreads();
 
-  // ---- softmax statistics per query head
-  for (int h = 0; h < G; ++h) {
-    float m = -INFINITY;
-    for (int j = tid; j < C; j += kH2OThreads) m = fmaxf(m, lg[h * C + j]);
+  // ---- softmax statistics per query head: merge the lanes' running (m, s)
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) red[wave][h] = m;
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h >= G) break;
+    float m = om[h], sm = os[h];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
+      const float mn = fmaxf(m, m2);
+      if (mn > -INFINITY) {
+        sm = sm * __builtin_amdgcn_exp2f(m - mn) + s2 * __builtin_amdgcn_exp2f(m2 - mn);
+        m = mn;
+      }
+    }
+    if (lane == 0) {
+      red[wave][h] = m;
+      red2[wave][h] = sm;
+    }
   }
   __syncthreads();
   if (tid < G) {
     float m = selfx[tid];
     for (int w = 0; w < WAVES; ++w) m = fmaxf(m, red[w][tid]);
-    Mh[tid] = m;
-  }
-  __syncthreads();
-  for (int h = 0; h < G; ++h) {
-    const float m = Mh[h];
-    float s = 0.f;
+    float sm = (m > -INFINITY && selfx[tid] > -INFINITY) ? __builtin_amdgcn_exp2f(selfx[tid] - m)
+                                                          : 0.f;
     if (m > -INFINITY)
-      for (int j = tid; j < C; j += kH2OThreads) s += __builtin_amdgcn_exp2f(lg[h * C + j] - m);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) red[wave][h] = s;
-  }
-  __syncthreads();
-  if (tid < G) {
-    const float m = Mh[tid];
-    float s = (m > -INFINITY && selfx[tid] > -INFINITY) ? __builtin_amdgcn_exp2f(selfx[tid] - m) : 0.f;
-    for (int w = 0; w < WAVES; ++w) s += red[w][tid];
-    iLh[tid] = s > 0.f ? 1.f / s : 0.f;
+      for (int w = 0; w < WAVES; ++w)
+        if (red[w][tid] > -INFINITY) sm += red2[w][tid] * __builtin_amdgcn_exp2f(red[w][tid] - m);
+    Mh[tid] = m;
+    iLh[tid] = sm > 0.f ? 1.f / sm : 0.f;
   }
   __syncthreads();
 
