@@ -176,7 +176,8 @@ int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* 
  * evicted (nullable) [B][Hkv]: evicted position or -1.  probs (nullable)
  * [B][Hq][C+1] fp32: this step's probabilities per slot (0 for empty slots)
  * and, last, the new token's own probability.
- * Requires C >= n_sink + n_recent, Hq/Hkv <= 16 and (Hq/Hkv) * C <= 12288.
+ * Requires C >= n_sink + n_recent, Hq/Hkv <= 16 and (Hq/Hkv + 1) * C <= 16384
+ * (the logits and the slot positions of one (sequence, KV head) sit in LDS).
  */
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
              void* v_cache, float* acc, int32_t* pos, const int64_t* t /* host [B] */, int B,

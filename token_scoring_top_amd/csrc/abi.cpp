@@ -217,7 +217,7 @@ int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, voi
   if (rc) return rc;
   if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
   const int G = Hq / Hkv;
-  if (G > 16 || C < 1 || (int64_t)G * C > 12288) return HUBKV_EINVAL;
+  if (G > 16 || C < 1 || (int64_t)(G + 1) * C > 16384) return HUBKV_EINVAL;
   if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > C) return HUBKV_EINVAL;
   if ((int64_t)B * Hkv > ((int64_t)1 << 30) || !isfinite(scale)) return HUBKV_EINVAL;
   H2OArgs a;

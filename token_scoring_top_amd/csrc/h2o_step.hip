@@ -37,6 +37,8 @@ __device__ __forceinline__ uint32_t asc_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ int G_of(const H2OArgs& a) { return a.Hq / a.Hkv; }
+
 template <typename T, int D>
 __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
@@ -47,7 +49,8 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   constexpr int LPR = D / EPL;              // lanes per slot row
   constexpr int RPW = 64 / LPR;             // rows per wave per sweep step
   constexpr int WAVES = kH2OThreads / 64;
-  extern __shared__ float lg[];  // [G][C] logits in log2 units
+  extern __shared__ float lg[];  // [G][C] logits in log2 units, then [C] positions
+  int32_t* pl = (int32_t*)(lg + G_of(a) * a.C);
   __shared__ float qs[kMaxG][D];
   __shared__ float red[WAVES][kMaxG], red2[WAVES][kMaxG];
   __shared__ float Mh[kMaxG], iLh[kMaxG], selfx[kMaxG];
@@ -79,19 +82,28 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     om[h] = -INFINITY;
     os[h] = 0.f;
   }
-  // kUnroll row groups per wave are loaded before any is reduced, so each
-  // wave keeps kUnroll 16-byte loads (and their positions) in flight
-  constexpr int kUnroll = 8;
-  for (int j0 = wave * RPW; j0 < C; j0 += WAVES * RPW * kUnroll) {
-    u32x4 raw[kUnroll];
-    int32_t pj[kUnroll];
+  // positions of the slots, staged in LDS with coalesced loads
+  for (int j = tid; j < C; j += kH2OThreads) pl[j] = P[j];
+  // row groups are software-pipelined: the next kUnroll groups' loads are in
+  // flight while the current kUnroll groups are reduced
+  constexpr int kUnroll = 4;
+  constexpr int kStep = WAVES * RPW * kUnroll;
+  u32x4 nxt[kUnroll];
+  auto load_group = [&](int j0, u32x4 (&dst)[kUnroll]) {
 #pragma unroll
     for (int uu = 0; uu < kUnroll; ++uu) {
       const int j = j0 + uu * WAVES * RPW + rsub;
       const int jc = j < C ? j : C - 1;  // past-the-end rows read the last slot, never stored
-      raw[uu] = *(const u32x4*)(Kc + (int64_t)jc * D + piece * EPL);
-      pj[uu] = P[jc];
+      dst[uu] = *(const u32x4*)(Kc + (int64_t)jc * D + piece * EPL);
     }
+  };
+  load_group(wave * RPW, nxt);
+  __syncthreads();  // positions staged
+  for (int j0 = wave * RPW; j0 < C; j0 += kStep) {
+    u32x4 raw[kUnroll];
+#pragma unroll
+    for (int uu = 0; uu < kUnroll; ++uu) raw[uu] = nxt[uu];
+    if (j0 + kStep < C) load_group(j0 + kStep, nxt);
 #pragma unroll
     for (int uu = 0; uu < kUnroll; ++uu) {
       const int j = j0 + uu * WAVES * RPW + rsub;
@@ -99,7 +111,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       float kv[EPL];
 #pragma unroll
       for (int x = 0; x < EPL; ++x) kv[x] = to_f<T>(e[x]);
-      const bool occ = pj[uu] >= 0;
+      const bool occ = j < C && pl[j] >= 0;
 #pragma unroll
       for (int h = 0; h < kMaxG; ++h) {
         if (h >= G) break;
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   unsigned long long best = ~0ull;
   int best_slot = -1, first_empty = 0x7fffffff;
   for (int j = tid; j < C; j += kH2OThreads) {
-    const int32_t pj = P[j];
+    const int32_t pj = pl[j];
     float add = 0.f;
     for (int h = 0; h < G; ++h) {
       const float p = pj >= 0 ? __builtin_amdgcn_exp2f(lg[h * C + j] - Mh[h]) * iLh[h] : 0.f;
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
 
 }  // namespace
 
-size_t h2o_lds_bytes(int G, int C) { return (size_t)G * C * sizeof(float); }
+size_t h2o_lds_bytes(int G, int C) { return (size_t)G * C * sizeof(float) + (size_t)C * sizeof(int32_t); }
 
 hipError_t launch_h2o_step(const void* q, const void* k_new, const void* v_new, int dtype,
                            void* k_cache, void* v_cache, float* acc, int32_t* pos,
