@@ -111,7 +111,7 @@ size_t hubkv_score_workspace(int B, const int64_t* seqlens, int L, int Hq, int H
   if (check_dtype_d(dtype, d) != HUBKV_OK) return 0;
   SeqTable st;
   if (B < 1 || B > kMaxSeqs || !seqlens) return 0;
-  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, dtype);
+  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, Hkv > 0 ? (Hq / Hkv) * W : 0, dtype);
   if (make_table(st, B, seqlens, chunk) != HUBKV_OK) return 0;
   if (check_score_shape(L, Hq, Hkv, W, st) != HUBKV_OK) return 0;
   return score_geometry(st, L, Hq, Hkv, W, d, dtype).bytes;
@@ -124,7 +124,7 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
   if (rc) return rc;
   SeqTable st;
   if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
-  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, dtype);
+  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, Hkv > 0 ? (Hq / Hkv) * W : 0, dtype);
   if ((rc = make_table(st, B, seqlens, chunk))) return rc;
   if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
   if (!isfinite(scale)) return HUBKV_EINVAL;

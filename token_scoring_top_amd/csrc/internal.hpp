@@ -53,9 +53,9 @@ struct ScoreGeom {
   size_t off_part1, off_rowstat, off_part2, off_ctl, bytes;  // rowstat: fp32 path only
 };
 
-// Chunk size the score path uses for these sequence lengths and `units`
-// (layers x KV heads) independent score problems.
-int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype);
+// Chunk size the score path uses for these sequence lengths, `units` (layers
+// x KV heads) independent score problems and `rows` (G * W) query rows each.
+int score_chunk(int B, const int64_t* seqlens, int64_t units, int rows, int dtype);
 
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype);
 

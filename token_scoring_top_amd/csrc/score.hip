@@ -52,7 +52,7 @@ struct ScoreArgs {
 // --------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype) {
+int score_chunk(int B, const int64_t* seqlens, int64_t units, int rows, int dtype) {
   if (dtype != 1) return kScoreChunkF32;
   // Chunks in multiples of 1024 keys, chosen to minimise the makespan
   // (rounds of kScoreGroups work-groups) x (chunk + a fixed start-up cost of
@@ -63,6 +63,10 @@ int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype) {
   int64_t mx = 0;
   for (int b = 0; b < B; ++b) mx = seqlens[b] > mx ? seqlens[b] : mx;
   if (units < 1) units = 1;
+  // work-groups of several 64-row groups are MFMA-heavy and want two waves
+  // per SIMD: a round then holds as many of them as fit two per SIMD
+  const int nrg = (rows + 63) / 64;
+  const int64_t per_round = nrg >= 2 ? kScoreGroups * (8 / nrg > 1 ? 8 / nrg : 1) : kScoreGroups;
   const int64_t top = (mx + kScoreChunkMfma - 1) / kScoreChunkMfma;
   int64_t best_c = kScoreChunkMfma, best_cost = INT64_MAX;
   for (int64_t m = 1; m <= top && m <= ((int64_t)1 << 20); ++m) {
@@ -70,7 +74,7 @@ int score_chunk(int B, const int64_t* seqlens, int64_t units, int dtype) {
     int64_t groups = 0;
     for (int b = 0; b < B; ++b) groups += (seqlens[b] + c - 1) / c;
     groups *= units;
-    const int64_t rounds = (groups + kScoreGroups - 1) / kScoreGroups;
+    const int64_t rounds = (groups + per_round - 1) / per_round;
     const int64_t cost = rounds * (c + kScoreStartKeys);
     if (cost < best_cost) {
       best_cost = cost;
