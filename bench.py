@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "b4f459670f6535fcd2bdc6a663acfc7fa9d06d03e99ff172af96996110e95449", "workload": 2,
-                 "fetch_bytes": 546507634, "write_bytes": 4858880}
+SCORE_TRAFFIC = {"sha256": "df22b0a8a2bc89e4646e80c6ae48788d6d71460823ab7fca5dc983892c23316d", "workload": 2,
+                 "fetch_bytes": 546593061, "write_bytes": 4350932}
 
 
 def _score_source_sha() -> str:
