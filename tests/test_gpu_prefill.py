@@ -53,6 +53,8 @@ SCORE_CASES = [
     ([3000, 700, 1200], 1, 32, 8, 64, 128, True),  # 256 rows, three sequences
     ([4100], 1, 4, 1, 128, 128, True),        # 512 rows, the largest group
     ([64], 1, 1, 1, 64, 128, True),           # window covers the whole sequence
+    ([2500, 900], 1, 8, 2, 48, 64, True),     # 192 rows (3 row groups), d = 64, ragged
+    ([1800], 1, 6, 1, 50, 128, False),        # 300 rows (5 row groups), no mask
 ]
 
 

@@ -130,25 +130,6 @@ __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const
 // completed (s_waitcnt vmcnt(0)), so no cache write-back or invalidation is
 // needed.
 // --------------------------------------------------------------------------
-// Shared K staging (row groups NRG >= 2): each stage holds 32 keys per row
-// group, rows padded to 2 D + 16 bytes so the lanes' 16-byte fragment reads
-// fall in distinct LDS banks.
-template <int D, int NRG>
-constexpr int stage_bytes() { return NRG > 1 ? 32 * NRG * (2 * D + 16) : 16; }
-
-// Keys per column-sum round in pass 2.  One row group: 32 KiB of LDS partial
-// sums, so a 4096-key chunk is a single round (K keeps streaming without a
-// barrier in between).  Several row groups: about 20 KiB of LDS per row group
-// in total (so small work-groups still share a compute unit), in whole stages.
-template <int D, int NRG>
-constexpr int sub_keys() {
-  if (NRG == 1) return 8192;
-  constexpr int sk = 32 * NRG;
-  constexpr int budget = (20 * 1024 * NRG < 150 * 1024 ? 20 * 1024 * NRG : 150 * 1024);
-  constexpr int n = (budget - stage_bytes<D, NRG>() - 4096) / (4 * NRG) / sk;
-  return sk * (n > 1 ? n : 1);
-}
-
 __device__ __forceinline__ void st_agent(float2* p, float2 v) {
   __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, v),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -260,7 +241,7 @@ __device__ __forceinline__ float tile_col_sums(const bf16x8 (&qf)[2][D / 16],
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
     acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][kk], kf[kk], acc[1], 0, 0, 0);
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  float ps[4];
   // re-read the normalisers every tile rather than holding 32 of them in
   // registers across the loop (the opaque offset keeps them from being hoisted)
   int moff = 4 * (lane >> 5);
@@ -289,11 +270,9 @@ __device__ __forceinline__ float tile_col_sums(const bf16x8 (&qf)[2][D / 16],
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float p = fast_exp2(fmaf(acc[qt][j], c2, -Mr[j]));
-      if constexpr (MASK)
-        ps[j & 3] += key <= Lr[j] ? p : 0.f;
-      else
-        ps[j & 3] += p;
+      float p = fast_exp2(fmaf(acc[qt][j], c2, -Mr[j]));
+      if constexpr (MASK) p = key <= Lr[j] ? p : 0.f;
+      ps[j & 3] = (qt == 0 && j < 4) ? p : ps[j & 3] + p;
     }
   }
   // MFMA(acc1) k-steps interleaved with the VALU work on acc0
@@ -332,17 +311,19 @@ __device__ __forceinline__ void tile_row_stats(const bf16x8 (&qf)[2][D / 16],
       for (int j = 0; j < 16; ++j)
         if (key0 + c_row(j, lane) > lim[qt]) acc[qt][j] = -INFINITY;
     }
-    float t4[4];
+    // IEEE maximum (v_maximum3_f32) needs no canonicalising of the MFMA
+    // results, unlike fmaxf; logits are finite or -inf here
+    float tmax = acc[qt][0];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      t4[e] = fmaxf(fmaxf(acc[qt][4 * e], acc[qt][4 * e + 1]),
-                    fmaxf(acc[qt][4 * e + 2], acc[qt][4 * e + 3]));
-    const float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    for (int j = 1; j < 16; ++j) tmax = __builtin_elementwise_maximum(tmax, acc[qt][j]);
     const float mn = fmaxf(m[qt], tmax * c2);
     const float mref = fmaxf(mn, -1.0e30f);  // all keys masked so far: stay at zero
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ps[j & 3] += fast_exp2(fmaf(acc[qt][j], c2, -mref));
+    for (int j = 0; j < 16; ++j) {
+      const float p = fast_exp2(fmaf(acc[qt][j], c2, -mref));
+      ps[j & 3] = j < 4 ? p : ps[j & 3] + p;
+    }
     s[qt] = fmaf(s[qt], fast_exp2(m[qt] - mref), (ps[0] + ps[1]) + (ps[2] + ps[3]));
     m[qt] = mn;
   }
@@ -378,53 +359,68 @@ __device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t first, int
   }
 }
 
-// Sweep [first, end) with the K tiles shared by the work-group's NRG row
-// groups (one wave each): per stage of 32 NRG keys every wave loads one 32-key
-// tile from global memory (whole 256-byte rows per load instruction) into
-// registers, the stage is written to LDS, and every wave then reduces all of
-// the stage's tiles for its own 64 query rows, reading its MFMA fragments from
-// LDS.  The next stage's global loads are in flight during that compute.
-// Each K byte is read from memory once per work-group instead of once per
-// row group.  Past-the-end rows load the last valid key and are masked by the
-// callers.  Called by every thread of the work-group.
-template <int D, int NRG, typename F>
-__device__ __forceinline__ void sweep_stages(const __bf16* Kh, int64_t first, int64_t end,
-                                             char* kst, int lane, int wave, F&& body) {
-  constexpr int ROWB = 2 * D + 16;
-  constexpr int PPR = 2 * D / 16;    // 16-byte pieces per key row
-  constexpr int PPL = 32 * PPR / 64;  // pieces per lane for one 32-key tile
-  constexpr int RPI = 64 / PPR;       // key rows per load instruction
-  constexpr int SK = 32 * NRG;
-  const int nst = __builtin_amdgcn_readfirstlane(
-      first < end ? (int)((end - first + SK - 1) / SK) : 0);
-  if (nst == 0) return;
-  const int prow = lane / PPR, pcol = lane % PPR;
-  u32x4 stg[PPL];
-  auto gload = [&](int64_t s0) {
+// Pass-2 prologue: fold every chunk's pass-1 partials of the unit into the
+// row normalisers M = m + log2(l), in chunk order (every work-group of the
+// unit computes the same values), and the last visible key of every row
+// (the whole sequence for padding rows), both into LDS.
+__device__ __forceinline__ void fold_row_norms(const float2* __restrict__ part1, const ScoreArgs& a,
+                                               const SeqTable& st, int lh, int b, int nch, int N,
+                                               int tid, int nthreads, float* mrow, int* rlim) {
+  const float2* pp = part1 + ((int64_t)lh * a.nchunk + st.tile_off[b]) * a.Mpad;
+  for (int r = tid; r < a.Mpad; r += nthreads) {
+    float mm = kMinit, ss = 0.f;
+    for (int cc = 0; cc < nch; cc += 8) {
+      float2 pv[8];
 #pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      int64_t key = s0 + 32 * wave + prow + RPI * i;
-      key = key < end ? key : end - 1;
-      stg[i] = *(const u32x4*)(Kh + key * D + pcol * 8);
+      for (int e = 0; e < 8; ++e)
+        pv[e] = cc + e < nch ? pp[(int64_t)(cc + e) * a.Mpad + r] : make_float2(kMinit, 0.f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (pv[e].y > 0.f) merge_ml(mm, ss, pv[e].x, pv[e].y);
     }
-  };
-  gload(first);
-  for (int si = 0; si < nst; ++si) {
-    const int64_t s0 = first + (int64_t)si * SK;
-    __syncthreads();  // the previous stage's readers are done
+    mrow[r] = (r < a.M && ss > 0.f) ? mm + __builtin_amdgcn_logf(ss) : INFINITY;
+    rlim[r] = row_limit(a, N, r, N - 1);
+  }
+}
+
+// Pass-2 epilogue: the work-group's {sum s, sum s ln s} (per-thread doubles)
+// are reduced, published for its chunk, and the unit's last chunk to count
+// in adds all chunks up in chunk order into the head statistics.
+template <int WAVES>
+__device__ __forceinline__ void finish_chunk_stats(double hs, double ha, double2* hred,
+                                                   double2* __restrict__ part2, int* done,
+                                                   const ScoreArgs& a, const SeqTable& st, int lh,
+                                                   int chunk_g, int b, int nch, int l, int g,
+                                                   double* __restrict__ stats, int tid, int lane,
+                                                   int wave) {
 #pragma unroll
-    for (int i = 0; i < PPL; ++i)
-      *(u32x4*)(kst + (32 * wave + prow + RPI * i) * ROWB + pcol * 16) = stg[i];
-    __syncthreads();
-    if (si + 1 < nst) gload(s0 + SK);
-    for (int t = 0; t < NRG; ++t) {
-      const int64_t key0 = s0 + 32 * t;
-      if (key0 >= end) break;
-      bf16x8 kf[D / 16];
-      const char* base = kst + (32 * t + (lane & 31)) * ROWB + 16 * (lane >> 5);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const bf16x8*)(base + 32 * kk);
-      body(kf, key0);
+  for (int off = 32; off >= 1; off >>= 1) {
+    hs += __shfl_xor(hs, off);
+    ha += __shfl_xor(ha, off);
+  }
+  if (lane == 0) hred[wave] = make_double2(hs, ha);
+  __syncthreads();
+  if (tid == 0) {
+    double S = 0.0, A = 0.0;
+    for (int w = 0; w < WAVES; ++w) {
+      S += hred[w].x;
+      A += hred[w].y;
+    }
+    double* p2w = (double*)&part2[(int64_t)lh * a.nchunk + chunk_g];
+    st_agent(p2w, S);
+    st_agent(p2w + 1, A);
+    wait_stores();
+    if (bump_agent(done) == nch - 1 && stats) {
+      // the unit's last chunk: head statistics, chunks added in order
+      double S2 = 0.0, A2 = 0.0;
+      const double* p2 = (const double*)(part2 + (int64_t)lh * a.nchunk + st.tile_off[b]);
+      for (int cc = 0; cc < nch; ++cc) {
+        S2 += ld_agent(p2 + 2 * cc);
+        A2 += ld_agent(p2 + 2 * cc + 1);
+      }
+      const int64_t su = (((int64_t)l * st.B + b) * a.Hkv + g) * 2;
+      stats[su] = S2;
+      stats[su + 1] = A2;
     }
   }
 }
@@ -452,10 +448,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
   const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
 
-  // several row groups share each K tile through LDS (see sweep_stages)
-  constexpr bool kShared = NRG > 1;
-  static_assert(!kShared || NKG == 1, "shared K staging expects one wave per row group");
-  __shared__ __attribute__((aligned(16))) char kst[stage_bytes<D, NRG>()];
+  static_assert(NRG == 1, "several row groups use score_pass_shared");
 
   bf16x8 qf[2][KS];
   load_q_frags<D>(qf, Q, a, st, l, g, b, rg, lane);
@@ -479,8 +472,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       else
         tile_row_stats<D, true>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
     };
-    if constexpr (kShared) sweep_stages<D, NRG>(Kh, key_begin, key_end, kst, lane, wave, body1);
-    else sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane, body1);
+    sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane, body1);
     // lanes l and l + 32 hold the same rows over different keys
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -507,7 +499,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
     // key0 + l % 32 and 16 rows of each query tile, so a column sum is a
     // lane-local sum plus one exchange between the two half-waves.
-    constexpr int kSub = sub_keys<D, NRG>();
+    constexpr int kSub = 8192;  // one round per 4096-key chunk
     __shared__ float cs[NRG][kSub];
     __shared__ double2 hred[WAVES];
     // row normalisers in LDS: a lane's 16 rows of a query tile are 4 runs of
@@ -516,25 +508,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     __shared__ __attribute__((aligned(16))) float mrow[64 * NRG];
     // last visible key of every row (the whole sequence for padding rows)
     __shared__ __attribute__((aligned(16))) int rlim[64 * NRG];
-    int* done2 = ctl;
-    // fold every chunk's pass-1 partials of this unit into the row
-    // normalisers M = m + log2(l), in chunk order (every work-group of the
-    // unit computes the same values)
-    const float2* pp = part1 + ((int64_t)lh * a.nchunk + st.tile_off[b]) * a.Mpad;
-    for (int r = tid; r < a.Mpad; r += TH) {
-      float mm = kMinit, ss = 0.f;
-      for (int cc = 0; cc < nch; cc += 8) {
-        float2 pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pv[e] = cc + e < nch ? pp[(int64_t)(cc + e) * a.Mpad + r] : make_float2(kMinit, 0.f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (pv[e].y > 0.f) merge_ml(mm, ss, pv[e].x, pv[e].y);
-      }
-      mrow[r] = (r < a.M && ss > 0.f) ? mm + __builtin_amdgcn_logf(ss) : INFINITY;
-      rlim[r] = row_limit(a, N, r, N - 1);
-    }
+    fold_row_norms(part1, a, st, lh, b, nch, N, tid, TH, mrow, rlim);
     __syncthreads();
     double hs = 0.0, ha = 0.0;
     float* so = s_out + (int64_t)lh * a.T + st.cu[b];
@@ -557,8 +531,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
         cv += __shfl_xor(cv, 32);
         if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
       };
-      if constexpr (kShared) sweep_stages<D, NRG>(Kh, sub0, sub1, kst, lane, wave, body2);
-      else sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane, body2);
+      sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane, body2);
       __syncthreads();
       for (int i = tid; i < sub1 - sub0; i += TH) {
         float v = cs[0][i];
@@ -570,39 +543,175 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       }
       __syncthreads();
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      hs += __shfl_xor(hs, off);
-      ha += __shfl_xor(ha, off);
-    }
-    if (lane == 0) hred[wave] = make_double2(hs, ha);
-    __syncthreads();
-    if (tid == 0) {
-      double S = 0.0, A = 0.0;
-      for (int w = 0; w < WAVES; ++w) {
-        S += hred[w].x;
-        A += hred[w].y;
-      }
-      double* p2w = (double*)&part2[(int64_t)lh * a.nchunk + chunk_g];
-      st_agent(p2w, S);
-      st_agent(p2w + 1, A);
-      wait_stores();
-      if (bump_agent(&done2[u]) == nch - 1 && stats) {
-        // the unit's last chunk: head statistics, chunks added in order
-        double S2 = 0.0, A2 = 0.0;
-        const double* p2 = (const double*)(part2 + (int64_t)lh * a.nchunk + st.tile_off[b]);
-        for (int cc = 0; cc < nch; ++cc) {
-          S2 += ld_agent(p2 + 2 * cc);
-          A2 += ld_agent(p2 + 2 * cc + 1);
-        }
-        const int64_t su = (((int64_t)l * st.B + b) * a.Hkv + g) * 2;
-        stats[su] = S2;
-        stats[su + 1] = A2;
-      }
-    }
+    finish_chunk_stats<WAVES>(hs, ha, hred, part2, ctl + u, a, st, lh, chunk_g, b, nch, l, g,
+                              stats, tid, lane, wave);
   }
 }
 
+// --------------------------------------------------------------------------
+// Several 64-row query groups (G * W > 64): the work-group's NRG waves (one
+// per row group) share every K tile.  Keys are processed in stages of 32
+// NRG; wave w brings tile w of the next stage straight from global memory
+// into LDS (global_load_lds_dwordx4: 16 bytes per lane, 1 KiB per
+// instruction, no staging registers) while all waves reduce the current
+// stage's tiles for their own rows, reading MFMA fragments from LDS.  Stages
+// are double-buffered, one barrier per stage.  Within a tile's LDS image,
+// 16-byte piece p of key row r sits at slot p ^ (r mod pieces-per-row), so
+// the 32 lanes that read the same piece of 32 rows spread over the banks.
+// Pass 2 writes each stage's per-row-group column sums to LDS (also double
+// buffered) and reduces them after the stage barrier.
+// --------------------------------------------------------------------------
+typedef const __attribute__((address_space(1))) void* gvoid_p;
+typedef __attribute__((address_space(3))) void* lvoid_p;
+
+template <int D, int NRG, int PHASE>
+__global__ __launch_bounds__(64 * NRG, 2) void score_pass_shared(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, SeqTable st, ScoreArgs a,
+    int* __restrict__ ctl, float2* __restrict__ part1, double2* __restrict__ part2,
+    float* __restrict__ s_out, double* __restrict__ stats) {
+  constexpr int TH = 64 * NRG;
+  constexpr int KS = D / 16;
+  constexpr int PPR = 2 * D / 16;  // 16-byte pieces per key row
+  constexpr int RB = 2 * D;        // key row bytes
+  constexpr int TILEB = 32 * RB;   // one 32-key tile
+  constexpr int RPI = 64 / PPR;    // key rows per DMA instruction
+  constexpr int NI = 32 / RPI;     // DMA instructions per tile
+  constexpr int SK = 32 * NRG;     // keys per stage
+  __shared__ __attribute__((aligned(1024))) char kbuf[2][NRG * TILEB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave;
+  const int lh = blockIdx.y, chunk_g = blockIdx.x;
+  const int b = seq_of_tile(st, chunk_g);
+  const int c = chunk_g - st.tile_off[b];
+  const int u = lh * st.B + b;
+  const int l = lh / a.Hkv, g = lh - l * a.Hkv;
+  const int nch = st.tile_off[b + 1] - st.tile_off[b];
+  const int N = (int)st.N[b];
+  const int64_t key_begin = (int64_t)c * a.chunk;
+  const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
+  const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
+  const int nst = __builtin_amdgcn_readfirstlane((int)((key_end - key_begin + SK - 1) / SK));
+
+  // wave w's tile of the stage at s0 into buffer `buf`; rows past the end
+  // load the last key (always in bounds) and are masked by the callers
+  const int drow = lane / PPR, dslot = lane % PPR;
+  auto dma = [&](int64_t s0, int buf) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + drow;
+      const int piece = dslot ^ (r & (PPR - 1));
+      int64_t key = s0 + 32 * wave + r;
+      key = key < key_end ? key : key_end - 1;
+      __builtin_amdgcn_global_load_lds((gvoid_p)(Kh + key * D + piece * 8),
+                                       (lvoid_p)(kbuf[buf] + wave * TILEB + i * 1024), 16, 0,
+                                       0);
+    }
+  };
+  // MFMA fragments of tile t: lane l takes row l % 32, pieces 2 kk + l / 32
+  auto frags = [&](int buf, int t, bf16x8 (&kf)[KS]) {
+    const int r = lane & 31;
+    const char* row = kbuf[buf] + t * TILEB + r * RB;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int piece = 2 * kk + (lane >> 5);
+      kf[kk] = *(const bf16x8*)(row + 16 * (piece ^ (r & (PPR - 1))));
+    }
+  };
+
+  if (nst > 0) dma(key_begin, 0);
+  bf16x8 qf[2][KS];
+  load_q_frags<D>(qf, Q, a, st, l, g, b, rg, lane);
+  const int last = (int)key_end - 1;
+  const int minlim = wave_min_limit(a, N, rg, lane, last);
+
+  if constexpr (PHASE == 1) {
+    __shared__ float2 red[64 * NRG];
+    int lim[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) lim[qt] = row_limit(a, N, rg * 64 + qt * 32 + (lane & 31), last);
+    float m[2] = {-INFINITY, -INFINITY}, sm[2] = {0.f, 0.f};
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int si = 0; si < nst; ++si) {
+      const int buf = si & 1;
+      const int64_t s0 = key_begin + (int64_t)si * SK;
+      if (si + 1 < nst) dma(s0 + SK, buf ^ 1);
+      for (int t = 0; t < NRG; ++t) {
+        const int64_t key0 = s0 + 32 * t;
+        if (key0 >= key_end) break;
+        bf16x8 kf[KS];
+        frags(buf, t, kf);
+        if ((int)key0 + 31 <= minlim)
+          tile_row_stats<D, false>(qf, kf, a.c2, (int)key0, lim, lane, m, sm);
+        else
+          tile_row_stats<D, true>(qf, kf, a.c2, (int)key0, lim, lane, m, sm);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    // lanes l and l + 32 hold the same rows over different keys
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m2 = __shfl_xor(m[qt], 32), s2 = __shfl_xor(sm[qt], 32);
+      const float mn = fmaxf(m[qt], m2);
+      const float mref = fmaxf(mn, -1.0e30f);
+      sm[qt] = sm[qt] * fast_exp2(m[qt] - mref) + s2 * fast_exp2(m2 - mref);
+      m[qt] = mn;
+      if (lane < 32) red[rg * 64 + qt * 32 + lane] = make_float2(fmaxf(m[qt], kMinit), sm[qt]);
+    }
+    __syncthreads();
+    for (int rl = tid; rl < a.Mpad; rl += TH)
+      part1[((int64_t)lh * a.nchunk + chunk_g) * a.Mpad + rl] = red[rl];
+    if (c == 0 && tid == 0) ctl[u] = 0;
+  } else {
+    __shared__ float csb[2][NRG][SK];
+    __shared__ double2 hred[NRG];
+    __shared__ __attribute__((aligned(16))) float mrow[64 * NRG];
+    __shared__ __attribute__((aligned(16))) int rlim[64 * NRG];
+    fold_row_norms(part1, a, st, lh, b, nch, N, tid, TH, mrow, rlim);
+    double hs = 0.0, ha = 0.0;
+    float* so = s_out + (int64_t)lh * a.T + st.cu[b];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int si = 0; si < nst; ++si) {
+      const int buf = si & 1;
+      const int64_t s0 = key_begin + (int64_t)si * SK;
+      if (si + 1 < nst) dma(s0 + SK, buf ^ 1);
+      for (int t = 0; t < NRG; ++t) {
+        const int64_t key0 = s0 + 32 * t;
+        if (key0 >= key_end) break;
+        bf16x8 kf[KS];
+        frags(buf, t, kf);
+        const int key = (int)key0 + (lane & 31);
+        float cv;
+        if ((int)key0 + 31 <= minlim)
+          cv = tile_col_sums<D, false>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                       last);
+        else
+          cv = tile_col_sums<D, true>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                      last);
+        cv += __shfl_xor(cv, 32);
+        if (lane < 32) csb[buf][rg][32 * t + lane] = cv;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // this stage's column sums over the row groups (csb[buf] is written
+      // again two stages on, after another barrier)
+      for (int i = tid; i < SK; i += TH) {
+        if (s0 + i >= key_end) break;
+        float v = csb[buf][0][i];
+#pragma unroll
+        for (int q = 1; q < NRG; ++q) v += csb[buf][q][i];
+        so[s0 + i] = v;
+        hs += (double)v;
+        if (v > 0.f) ha += (double)v * (double)(__builtin_amdgcn_logf(v) * kLn2);
+      }
+    }
+    finish_chunk_stats<NRG>(hs, ha, hred, part2, ctl + u, a, st, lh, chunk_g, b, nch, l, g, stats,
+                            tid, lane, wave);
+  }
+}
 
 // --------------------------------------------------------------------------
 // fp32 VALU path: one key per thread, query rows staged through LDS in
@@ -810,19 +919,36 @@ hipError_t run_mfma(const void* q, const void* k, const SeqTable& st, const Scor
   return hipGetLastError();
 }
 
+template <int D, int NRG>
+hipError_t run_shared(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
+                      char* ws, const ScoreGeom& geo, float* s, double* stats,
+                      hipStream_t stream) {
+  int* ctl = (int*)(ws + geo.off_ctl);
+  const dim3 grid(a.nchunk, a.L * a.Hkv), block(64 * NRG);
+  float2* part1 = (float2*)(ws + geo.off_part1);
+  double2* part2 = (double2*)(ws + geo.off_part2);
+  hipLaunchKernelGGL((score_pass_shared<D, NRG, 1>), grid, block, 0, stream, (const __bf16*)q,
+                     (const __bf16*)k, st, a, ctl, part1, part2, s, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((score_pass_shared<D, NRG, 2>), grid, block, 0, stream, (const __bf16*)q,
+                     (const __bf16*)k, st, a, ctl, part1, part2, s, stats);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dispatch_mfma(const void* q, const void* k, const SeqTable& st, const ScoreArgs& a,
                          char* ws, const ScoreGeom& geo, float* s, double* stats,
                          hipStream_t stream) {
   switch (a.Mpad / 64) {
     case 1: return run_mfma<D, 1, 4>(q, k, st, a, ws, geo, s, stats, stream);
-    case 2: return run_mfma<D, 2, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 3: return run_mfma<D, 3, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 4: return run_mfma<D, 4, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 5: return run_mfma<D, 5, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 6: return run_mfma<D, 6, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 7: return run_mfma<D, 7, 1>(q, k, st, a, ws, geo, s, stats, stream);
-    case 8: return run_mfma<D, 8, 1>(q, k, st, a, ws, geo, s, stats, stream);
+    case 2: return run_shared<D, 2>(q, k, st, a, ws, geo, s, stats, stream);
+    case 3: return run_shared<D, 3>(q, k, st, a, ws, geo, s, stats, stream);
+    case 4: return run_shared<D, 4>(q, k, st, a, ws, geo, s, stats, stream);
+    case 5: return run_shared<D, 5>(q, k, st, a, ws, geo, s, stats, stream);
+    case 6: return run_shared<D, 6>(q, k, st, a, ws, geo, s, stats, stream);
+    case 7: return run_shared<D, 7>(q, k, st, a, ws, geo, s, stats, stream);
+    case 8: return run_shared<D, 8>(q, k, st, a, ws, geo, s, stats, stream);
     default: return hipErrorInvalidValue;  // G*W > 512 is rejected before launch
   }
 }
