@@ -63,7 +63,7 @@ def lib():
                                   C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.orc_h2o_step.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _i32p, _i64p, C.c_int,
                                    C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_double,
-                                   C.c_int, _i32p, C.c_void_p, C.c_void_p]
+                                   C.c_int, _i32p, C.c_void_p, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -157,9 +157,10 @@ def compact(k_in, v_in, idx, seqlens, kept):
 
 
 def h2o_step(state: dict, q, k_new, v_new, t, scale, n_sink=0, n_recent=0, include_self=0,
-             want_probs=False, want_margin=False):
+             want_probs=False, want_margin=False, want_out=False):
     """One streaming step in place on state = {K, V [B][Hkv][C][d], acc, pos}.
-    Returns evicted [B][Hkv] (and probs [B][Hq][C+1], margin [B][Hkv] on request)."""
+    Returns evicted [B][Hkv] (and probs [B][Hq][C+1], margin [B][Hkv], the
+    attention output [B][Hq][d] on request, in that order)."""
     K, V, acc, pos = state["K"], state["V"], state["acc"], state["pos"]
     for a, dt in ((K, np.float32), (V, np.float32), (acc, np.float32), (pos, np.int32)):
         assert a.dtype == dt and a.flags.c_contiguous
@@ -170,16 +171,20 @@ def h2o_step(state: dict, q, k_new, v_new, t, scale, n_sink=0, n_recent=0, inclu
     ev = np.zeros((B, Hkv), np.int32)
     probs = np.zeros((B, Hq, Cs + 1), np.float32) if want_probs else None
     margin = np.zeros((B, Hkv), np.float32) if want_margin else None
+    att = np.zeros((B, Hq, d), np.float32) if want_out else None
     _check(lib().orc_h2o_step(q, _c(k_new, np.float32), _c(v_new, np.float32), K, V, acc, pos, tt,
                               B, Hq, Hkv, d, Cs, int(n_sink), int(n_recent), float(scale),
                               int(include_self), ev,
                               probs.ctypes.data if probs is not None else None,
-                              margin.ctypes.data if margin is not None else None))
+                              margin.ctypes.data if margin is not None else None,
+                              att.ctypes.data if att is not None else None))
     out = [ev]
     if want_probs:
         out.append(probs)
     if want_margin:
         out.append(margin)
+    if want_out:
+        out.append(att)
     return out[0] if len(out) == 1 else tuple(out)
 
 

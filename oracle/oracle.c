@@ -38,7 +38,9 @@
  *       new token is added (optionally including it), the new token enters
  *       with accumulated score 0 (or its own probability), and when the cache
  *       is over capacity the lowest accumulated score among tokens outside
- *       the sink and recent windows is evicted, ties to the oldest position.
+ *       the sink and recent windows is evicted, ties to the oldest position;
+ *   R11 the H2O step's attention output uses those same probabilities on the
+ *       values of the same tokens (before the new token is inserted).
  */
 #include <math.h>
 #include <stdint.h>
@@ -382,11 +384,18 @@ int orc_compact(const void* k_in, const void* v_in, const int32_t* idx, int elem
  * [B][Hq][C+1] (last entry: the new token's own probability, 0 unless
  * include_self); margin (nullable) [B][Hkv]: relative gap between the two
  * smallest candidate accumulated scores (+inf with fewer than two).
+ * out (nullable) [B][Hq][d]: the step's attention output, reading R11 --
+ *   the KV-cache page's decode attention (section 1.1) restricted to the
+ *   retained tokens as in the H2O page's problem statement (evicted tokens
+ *   leave the normaliser): out_h = sum over occupied slots of p_h(slot) *
+ *   v_slot, plus p_h(new) * v_new when include_self, with the same p_h that
+ *   are added to the accumulated scores, on the cache as it was before the
+ *   new token is inserted.
  * ------------------------------------------------------------------------ */
 int orc_h2o_step(const float* q, const float* knew, const float* vnew, float* kc, float* vc,
                  float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv, int d, int C,
                  int n_sink, int n_recent, double scale, int include_self, int32_t* evicted,
-                 float* probs, float* margin) {
+                 float* probs, float* margin, float* out) {
   if (Hq % Hkv || C < 1 || n_sink < 0 || n_recent < 0 || C < n_sink + n_recent) return ORC_EINVAL;
   const int G = Hq / Hkv;
   const int units = B * Hkv;
@@ -434,6 +443,16 @@ int orc_h2o_step(const float* q, const float* knew, const float* vnew, float* kc
       const double ps = include_self ? exp(x[C] - m) / lsum : 0.0;
       self_add += ps;
       if (pr) pr[C] = (float)ps;
+      if (out) {
+        float* oh = out + ((int64_t)b * Hq + h) * d;
+        for (int e = 0; e < d; ++e) {
+          double o = 0.0;
+          for (int j = 0; j < C; ++j)
+            if (P[j] >= 0) o += exp(x[j] - m) / lsum * (double)V[(int64_t)j * d + e];
+          if (include_self) o += ps * (double)vn[e];
+          oh[e] = (float)o;
+        }
+      }
     }
     for (int j = 0; j < C; ++j)
       if (P[j] >= 0) A[j] = (float)((double)A[j] + add[j]);

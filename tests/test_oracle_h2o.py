@@ -139,6 +139,109 @@ def test_step_probabilities_are_library_softmax():
             np.testing.assert_allclose(pr[b, h, :w.C], ref, rtol=1e-6, atol=1e-12)
 
 
+def _torch_attention(q, k, v, scale, mask):
+    """torch's scaled_dot_product_attention in float64 on the CPU:
+    q [H][Lq][d], k/v [H][Lk][d], mask [Lq][Lk] boolean (True = attend)."""
+    import torch
+    f = torch.nn.functional.scaled_dot_product_attention
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    return f(T(q)[None], T(k)[None], T(v)[None], attn_mask=torch.from_numpy(mask),
+             scale=float(scale))[0].numpy()
+
+
+@pytest.mark.parametrize("include_self", [0, 1])
+def test_attention_output_unbounded_is_causal_attention(include_self):
+    # KV-cache page, section 1.1: decode attention of token t is the softmax of
+    # its scaled query against every key so far, applied to the values.  With
+    # room for every token no eviction happens, so the step outputs are the
+    # rows of causal attention (strictly causal without self-attention), with
+    # KV head h // G serving query head h.
+    N, B, Hq, Hkv, d = 40, 2, 4, 2, 16
+    G = Hq // Hkv
+    q, k, v = _stream(N, B, Hq, Hkv, d, 61 + include_self)
+    st = oracle.empty_state(B, Hkv, N, d)
+    outs = []
+    for t in range(N):
+        ev, o = oracle.h2o_step(st, q[t], k[t], v[t], t, 0.3, 0, 0, include_self, want_out=True)
+        assert (ev == -1).all()
+        outs.append(o)
+    outs = np.array(outs)                                 # [N][B][Hq][d]
+    mask = np.tril(np.ones((N, N), bool), 0 if include_self else -1)
+    if not include_self:
+        mask[0, 0] = True                                 # row 0 is checked separately below
+    for b in range(B):
+        Kr = np.repeat(k[:, b].transpose(1, 0, 2), G, axis=0)   # [Hq][N][d]
+        Vr = np.repeat(v[:, b].transpose(1, 0, 2), G, axis=0)
+        ref = _torch_attention(q[:, b].transpose(1, 0, 2), Kr, Vr, 0.3, mask)
+        got = outs[:, b].transpose(1, 0, 2)
+        lo = 0 if include_self else 1
+        np.testing.assert_allclose(got[:, lo:], ref[:, lo:], rtol=1e-5, atol=1e-6)
+    if not include_self:
+        assert (outs[0] == 0).all()                       # nothing to attend to yet
+
+
+def test_attention_output_over_retained_tokens():
+    # H2O page, problem statement: an evicted token drops out of the keys and
+    # of the normaliser.  Each step's output is attention over the tokens the
+    # cache held before the step (plus the new token when it attends to
+    # itself), whatever slots they sit in.
+    B, Hq, Hkv, d, C = 2, 4, 2, 8, 11
+    G = Hq // Hkv
+    for inc in (0, 1):
+        q, k, v = _stream(60, B, Hq, Hkv, d, 71 + inc)
+        st = oracle.empty_state(B, Hkv, C, d)
+        for t in range(60):
+            before = {kk: vv.copy() for kk, vv in st.items()}
+            _, o = oracle.h2o_step(st, q[t], k[t], v[t], t, 0.4, 1, 3, inc, want_out=True)
+            if t == 0 and not inc:
+                continue
+            for b in range(B):
+                for g in range(Hkv):
+                    keys = np.concatenate([before["K"][b, g], k[t, b, g][None]])
+                    vals = np.concatenate([before["V"][b, g], v[t, b, g][None]])
+                    m = np.concatenate([before["pos"][b, g] >= 0, [bool(inc)]])[None]
+                    hs = slice(g * G, (g + 1) * G)
+                    ref = _torch_attention(q[t, b, hs][:, None], np.repeat(keys[None], G, 0),
+                                           np.repeat(vals[None], G, 0), 0.4, m)[:, 0]
+                    np.testing.assert_allclose(o[b, hs], ref, rtol=1e-5, atol=1e-6)
+
+
+def test_attention_output_ignores_empty_slot_contents():
+    # empty slots hold no token: their K/V rows (NaN here) never reach the output
+    B, Hq, Hkv, d, C = 1, 2, 1, 8, 16
+    q, k, v = _stream(6, B, Hq, Hkv, d, 81)
+    clean = oracle.empty_state(B, Hkv, C, d)
+    dirty = oracle.empty_state(B, Hkv, C, d)
+    dirty["K"][:] = np.nan
+    dirty["V"][:] = np.nan
+    for t in range(6):
+        _, oc = oracle.h2o_step(clean, q[t], k[t], v[t], t, 0.3, 0, 0, 1, want_out=True)
+        _, od = oracle.h2o_step(dirty, q[t], k[t], v[t], t, 0.3, 0, 0, 1, want_out=True)
+        np.testing.assert_array_equal(oc, od)
+
+
+def test_attention_output_is_convex_combination():
+    # probabilities sum to one: identical value rows come back unchanged, and a
+    # value ramp over positions returns the expected position under the softmax
+    B, Hq, Hkv, d, C = 1, 3, 1, 4, 9
+    q, k, _ = _stream(30, B, Hq, Hkv, d, 91)
+    vconst = np.broadcast_to(np.array([1.5, -2.0, 0.25, 3.0], np.float32), (30, B, Hkv, d)).copy()
+    st = oracle.empty_state(B, Hkv, C, d)
+    for t in range(30):
+        _, o = oracle.h2o_step(st, q[t], k[t], vconst[t], t, 0.5, 1, 2, 1, want_out=True)
+        np.testing.assert_allclose(o[0], np.broadcast_to(vconst[0, 0, 0], (Hq, d)), rtol=1e-6)
+    vramp = np.zeros((30, B, Hkv, d), np.float32)
+    vramp[:, 0, 0, 0] = np.arange(30)
+    st = oracle.empty_state(B, Hkv, C, d)
+    for t in range(30):
+        pos_before = st["pos"][0, 0].copy()
+        _, pr, o = oracle.h2o_step(st, q[t], k[t], vramp[t], t, 0.5, 1, 2, 1, want_probs=True,
+                                   want_out=True)
+        w = np.concatenate([np.maximum(pos_before, 0), [t]]).astype(np.float64)
+        np.testing.assert_allclose(o[0, :, 0], pr[0].astype(np.float64) @ w, rtol=1e-5, atol=1e-6)
+        assert np.all(o[0, :, 1:] == 0)
+
+
 def test_protected_windows_never_evicted():
     B, Hq, Hkv, d, C, ns, nr = 1, 2, 2, 8, 12, 3, 5
     q, k, v = _stream(80, B, Hq, Hkv, d, 21)

@@ -45,6 +45,13 @@ MUTANTS = {
     "h2o-evict-newest-on-tie": ("(aj == best && pj < bpos)", "(aj == best && pj > bpos)"),
     "h2o-recent-off-by-one": ("if (pj < n_sink || pj > tt - n_recent) continue;",
                               "if (pj < n_sink || pj >= tt - n_recent) continue;"),
+    "h2o-out-self-dropped": ("if (include_self) o += ps * (double)vn[e];", ""),
+    "h2o-out-keys-for-values": ("o += exp(x[j] - m) / lsum * (double)V[(int64_t)j * d + e];",
+                                "o += exp(x[j] - m) / lsum * (double)K[(int64_t)j * d + e];"),
+    "h2o-out-unnormalised": ("o += exp(x[j] - m) / lsum * (double)V[(int64_t)j * d + e];",
+                             "o += exp(x[j] - m) * (double)V[(int64_t)j * d + e];"),
+    "h2o-out-empty-slots-included": ("if (P[j] >= 0) o += exp(x[j] - m)",
+                                     "o += exp(x[j] - m)"),
     "h2o-no-acc-update": ("if (P[j] >= 0) A[j] = (float)((double)A[j] + add[j]);",
                           "if (P[j] >= 0) A[j] = A[j];"),
 }
