@@ -93,13 +93,17 @@ def score_flops(w):
     return 2.0 * w.L * w.Hq * w.W * w.T * w.d
 
 
-def h2o_step_bytes(w, elem):
+def h2o_step_bytes(w, elem, with_out=False):
     """Algorithmic HBM bytes of one h2o_step launch: every retained K row read,
     acc read and written, pos read, the query, the new K/V rows read, and one
-    slot's K/V/acc/pos written per (sequence, KV head)."""
+    slot's K/V/acc/pos written per (sequence, KV head).  With the attention
+    output, every retained V row is read too and the fp32 output written."""
     B, Hkv, Hq, d, C = w.B, w.Hkv, w.Hq, w.d, w.C
-    return (B * Hkv * C * (d * elem + 4 + 4 + 4) + B * Hq * d * elem
-            + B * Hkv * (2 * d * elem) + B * Hkv * (2 * d * elem + 8))
+    n = (B * Hkv * C * (d * elem + 4 + 4 + 4) + B * Hq * d * elem
+         + B * Hkv * (2 * d * elem) + B * Hkv * (2 * d * elem + 8))
+    if with_out:
+        n += B * Hkv * C * d * elem + B * Hq * d * 4
+    return n
 
 
 def bench_decode(args, w):
@@ -120,6 +124,7 @@ def bench_decode(args, w):
     acc = torch.zeros((B, Hkv, C), dtype=torch.float32, device=dev)
     pos = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
     ev = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if args.attn_out else None
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * w.wid)
     stream = torch.cuda.current_stream()
@@ -141,7 +146,7 @@ def bench_decode(args, w):
                 if evs is not None:
                     evs[t - t0][0].record(stream)
                 hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t, w.scale, w.n_sink, w.recent,
-                            bool(w.include_self), evicted=ev, stream=stream)
+                            bool(w.include_self), evicted=ev, out=o, stream=stream)
                 if evs is not None:
                     evs[t - t0][1].record(stream)
                 t += 1
@@ -156,7 +161,7 @@ def bench_decode(args, w):
     t0 = time.perf_counter()
     for i in range(steps):
         hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, stream=stream)
+                    bool(w.include_self), evicted=ev, out=o, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     t += steps
@@ -168,12 +173,12 @@ def bench_decode(args, w):
     for i in range(steps):
         evs[i][0].record(stream)
         hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, stream=stream)
+                    bool(w.include_self), evicted=ev, out=o, stream=stream)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     t += steps
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    nbytes = h2o_step_bytes(w, elem)
+    nbytes = h2o_step_bytes(w, elem, o is not None)
     ach = nbytes / (k_ms / 1e3) / 1e9
 
     cpu = None
@@ -191,7 +196,7 @@ def bench_decode(args, w):
         reps, tc0 = 0, time.perf_counter()
         while reps < 64:
             oracle.h2o_step(state, qs[reps], ks[reps], vs[reps], t + reps, w.scale, w.n_sink,
-                            w.recent, w.include_self)
+                            w.recent, w.include_self, want_out=o is not None)
             reps += 1
             if time.perf_counter() - tc0 >= args.cpu_budget_s:
                 break
@@ -216,7 +221,7 @@ def bench_decode(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "heavy": w.heavy,
                    "recent": w.recent, "prompt_steps_untimed": w.prompt,
-                   "parallelism": "none (1 GPU)"},
+                   "attention_output": o is not None, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": "h2o_step",
                      "kernels": "h2o_step_kernel", "algorithmic_bytes": nbytes},
@@ -237,6 +242,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--attn-out", action="store_true",
+                    help="decode workload: h2o_step also writes the attention output")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "

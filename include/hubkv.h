@@ -176,14 +176,23 @@ int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* 
  * evicted (nullable) [B][Hkv]: evicted position or -1.  probs (nullable)
  * [B][Hq][C+1] fp32: this step's probabilities per slot (0 for empty slots)
  * and, last, the new token's own probability.
+ * out (nullable) [B][Hq][d] fp32: the step's attention output -- the decode
+ * attention of the KV-cache page (section 1.1) over the retained tokens only
+ * (H2O breakdown page, problem statement: evicted tokens leave the
+ * normaliser): out[b][h] = sum over occupied slots of p_h(slot) *
+ * v_cache[b][g][slot], plus p_h(new) * v_new[b][g] when include_self, with
+ * the same p_h that are added to acc, on the cache before the new token is
+ * written.  All zeros when there is nothing to attend to.
  * Requires C >= n_sink + n_recent, Hq/Hkv <= 16 and (Hq/Hkv + 1) * C <= 16384
  * (the logits and the slot positions of one (sequence, KV head) sit in LDS).
+ * Buffers must not overlap (out, probs and evicted are written while the
+ * caches are read).
  */
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
              void* v_cache, float* acc, int32_t* pos, const int64_t* t /* host [B] */, int B,
              int Hq, int Hkv, int d, int C, int n_sink, int n_recent, float scale,
              int include_self, int32_t* evicted /* nullable */, float* probs /* nullable */,
-             void* stream);
+             float* out /* nullable */, void* stream);
 
 /* Number of protected positions of a sequence of length N (host helper). */
 int64_t hubkv_protected_count(int64_t N, int n_sink, int n_recent);

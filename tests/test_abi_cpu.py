@@ -145,7 +145,7 @@ def test_h2o_step_validation():
 
     def call(C_=64, ns=0, nr=8, Hq=4, Hkv=4, t=(100,), d=128, dt=1, acc=P, scale=0.1):
         return L.h2o_step(P, P, P, dt, P, P, acc, P, a64(list(t)), len(t), Hq, Hkv, d, C_, ns, nr,
-                          scale, 0, None, None, None)
+                          scale, 0, None, None, None, None)
 
     assert call(ns=60, nr=8) == EINVAL       # protected windows exceed the capacity
     assert call(Hq=6) == EINVAL

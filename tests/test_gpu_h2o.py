@@ -7,6 +7,13 @@
 * Free-running streams on small shapes: the evicted positions agree step by
   step; where they first diverge the oracle must report a near-tie.
 * The literal budget-3 run of the greedy algorithm keeps the first 3 tokens.
+* The optional attention output (decode attention over the retained tokens):
+  on the full decode shape, on partly empty caches whose empty rows hold NaN,
+  for every group size class (G = 1, 2, 3, 8, 16, the last with the largest
+  LDS footprint) and along free-running streams.  Error bar: |out - oracle| <=
+  tol * sum_slot p(slot) |v_slot| (the size of the convex combination), tol
+  1e-5 for fp32 inputs and 2e-2 for bf16 inputs (with a 1e-4 diagnostic: the
+  arithmetic is fp32 on exact bf16 values).
 """
 import json
 import os
@@ -52,6 +59,36 @@ def _gpu_step(ds, q, kn, vn, t, w, n_sink, n_recent, include_self, dtype, want_p
                      ds["acc"], ds["pos"], t, w.scale, n_sink, n_recent, include_self, probs=probs)
     torch.cuda.synchronize()
     return ev.cpu().numpy(), (probs.cpu().numpy() if want_probs else None)
+
+
+def _gpu_step_out(ds, q, kn, vn, t, w, n_sink, n_recent, include_self, dtype):
+    B, Hq, d = q.shape
+    probs = torch.zeros((B, Hq, w.C + 1), dtype=torch.float32, device="cuda")
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    ev = hk.h2o_step(to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), ds["K"], ds["V"],
+                     ds["acc"], ds["pos"], t, w.scale, n_sink, n_recent, include_self,
+                     probs=probs, out=out)
+    torch.cuda.synchronize()
+    return ev.cpu().numpy(), probs.cpu().numpy(), out.cpu().numpy()
+
+
+def _out_err(o_g, o_o, pr_o, V, vn, pos):
+    """max over (b, h, e) of |o_g - o_o| / sum_slot p |v_slot| (the oracle's p;
+    empty slots carry p = 0 and are masked out of V)."""
+    B, Hq, d = o_o.shape
+    Hkv = V.shape[1]
+    G = Hq // Hkv
+    Va = np.where((pos >= 0)[..., None], np.abs(V.astype(np.float64)), 0.0)
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            scale = pr_o[b, h, :-1].astype(np.float64) @ Va[b, g] + \
+                pr_o[b, h, -1] * np.abs(vn[b, g].astype(np.float64))
+            e = np.abs(o_g[b, h].astype(np.float64) - o_o[b, h]) / np.maximum(scale, 1e-30)
+            worst = max(worst, float(e.max()))
+    assert np.isfinite(o_g).all()
+    return worst
 
 
 def _compare_step(ds, st_o, ev_g, ev_o, pr_g, pr_o, margin, tol, dtype):
@@ -169,3 +206,106 @@ def test_literal_budget3_algorithm1_on_gpu():
         pos_g = ds["pos"].cpu().numpy()
         for h in range(w.Hkv):
             assert sorted(pos_g[0, h].tolist()) == gold["final_set"]
+
+
+@pytest.mark.parametrize("include_self", [0, 1])
+def test_attention_output_full_decode_shape(include_self):
+    w = S.workload(4)
+    t = w.prompt + 9
+    note("  drawing a 16 x 32 x 4096-slot state")
+    st = S.decode_random_state(w, t=t, seed=21 + include_self)
+    ds = _dev_state(st, w.dtype)
+    ev_g, pr_g, o_g = _gpu_step_out(ds, st["q"], st["k_new"], st["v_new"], t, w, w.n_sink,
+                                    w.recent, include_self, w.dtype)
+    st_o = {k: st[k].copy() for k in ("K", "V", "acc", "pos")}
+    note("  oracle step")
+    ev_o, pr_o, mg, o_o = oracle.h2o_step(st_o, st["q"], st["k_new"], st["v_new"], t, w.scale,
+                                          w.n_sink, w.recent, include_self, want_probs=True,
+                                          want_margin=True, want_out=True)
+    err = _out_err(o_g, o_o, pr_o, st["V"], st["v_new"], st["pos"])
+    assert err < 2e-2
+    assert err < 1e-4, err
+    # the output does not disturb the step itself
+    _compare_step(ds, st_o, ev_g, ev_o, pr_g, pr_o, mg, 2e-2, w.dtype)
+
+
+@pytest.mark.parametrize("dtype,d,G,C", [("f32", 64, 1, 64), ("bf16", 128, 2, 64),
+                                         ("bf16", 128, 3, 96), ("f32", 128, 8, 200),
+                                         ("bf16", 64, 8, 130), ("bf16", 128, 16, 960),
+                                         ("f32", 64, 16, 300)])
+def test_attention_output_group_sizes_with_empty_slots(dtype, d, G, C):
+    # a quarter of the slots are empty and their K/V rows hold NaN: they must
+    # stay out of the logits, the normaliser and the output
+    rec = min(24, C // 4)
+    w = S.workload(4).with_(B=3, Hkv=2, Hq=2 * G, d=d, heavy=C - rec, recent=rec, dtype=dtype,
+                            n_sink=2)
+    t = 3 * C
+    fill = C - C // 4
+    st = S.decode_random_state(w, t=t, seed=G * 7 + d, fill=fill)
+    empty = st["pos"] < 0
+    st["K"][empty] = np.nan
+    st["V"][empty] = np.nan
+    ds = _dev_state(st, dtype)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    for inc in (0, 1):
+        ds2 = {k: v.clone() for k, v in ds.items()}
+        ev_g, pr_g, o_g = _gpu_step_out(ds2, st["q"], st["k_new"], st["v_new"], t, w, 2, rec,
+                                        inc, dtype)
+        st_o = {k: st[k].copy() for k in ("K", "V", "acc", "pos")}
+        ev_o, pr_o, o_o = oracle.h2o_step(st_o, st["q"], st["k_new"], st["v_new"], t, w.scale,
+                                          2, rec, inc, want_probs=True, want_out=True)
+        assert (ev_o == -1).all() and (ev_g == -1).all()
+        err = _out_err(o_g, o_o, pr_o, np.nan_to_num(st["V"]), st["v_new"], st["pos"])
+        assert err < tol, err
+        if dtype == "bf16":
+            assert err < 1e-4, err
+
+
+def test_attention_output_empty_cache():
+    # nothing cached: the output is v_new when the token attends to itself,
+    # zeros otherwise
+    w = S.workload(4).with_(B=2, Hkv=2, Hq=4, d=128, heavy=16, recent=16, dtype="f32", n_sink=0)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 128), dtype=np.float32)
+    kn = rng.standard_normal((2, 2, 128), dtype=np.float32)
+    vn = rng.standard_normal((2, 2, 128), dtype=np.float32)
+    for inc in (0, 1):
+        ds = _dev_state(oracle.empty_state(2, 2, w.C, 128), "f32")
+        _, _, o_g = _gpu_step_out(ds, q, kn, vn, 0, w, 0, 16, inc, "f32")
+        want = np.repeat(vn, 2, axis=1) if inc else np.zeros_like(o_g)
+        np.testing.assert_array_equal(o_g, want)
+
+
+@pytest.mark.parametrize("dtype,include_self", [("f32", 1), ("bf16", 0)])
+def test_attention_output_free_running_stream(dtype, include_self):
+    w = S.workload(4).with_(B=2, Hq=8, Hkv=2, d=64, heavy=24, recent=16, dtype=dtype)
+    B, Hkv, Hq, d, Cs = w.B, w.Hkv, w.Hq, w.d, w.C
+    steps = 120
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((steps, B, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((steps, B, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((steps, B, Hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = S.round_bf16(q), S.round_bf16(k), S.round_bf16(v)
+    st_o = oracle.empty_state(B, Hkv, Cs, d)
+    ds = _dev_state(st_o, dtype)
+    diverged = np.zeros((B, Hkv), bool)
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    G = Hq // Hkv
+    for t in range(steps):
+        V_before, pos_before = st_o["V"].copy(), st_o["pos"].copy()
+        ev_g, _, o_g = _gpu_step_out(ds, q[t], k[t], v[t], t, w, 2, 16, include_self, dtype)
+        ev_o, pr_o, mg, o_o = oracle.h2o_step(st_o, q[t], k[t], v[t], t, w.scale, 2, 16,
+                                              include_self, want_probs=True, want_margin=True,
+                                              want_out=True)
+        if t == 0 and not include_self:
+            assert (o_g == 0).all()
+        else:
+            # units whose caches already differ are skipped
+            keep = np.repeat(~diverged, G, axis=1)
+            o_gm = np.where(keep[..., None], o_g, o_o)
+            assert _out_err(o_gm, o_o, pr_o, V_before, v[t], pos_before) < tol
+        newly = (ev_g != ev_o) & ~diverged
+        assert np.all(mg[newly] <= 1e-4), f"step {t}: divergence without a near-tie"
+        diverged |= newly
+    assert diverged.mean() <= 0.5

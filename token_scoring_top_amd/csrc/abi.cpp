@@ -212,7 +212,7 @@ int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* 
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
              void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
              int d, int C, int n_sink, int n_recent, float scale, int include_self,
-             int32_t* evicted, float* probs, void* stream) {
+             int32_t* evicted, float* probs, float* out, void* stream) {
   int rc = check_dtype_d(dtype, d);
   if (rc) return rc;
   if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
@@ -230,7 +230,9 @@ int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, voi
   if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(acc, 4) || !aligned(pos, 4))
     return HUBKV_EALIGN;
-  if ((evicted && !aligned(evicted, 4)) || (probs && !aligned(probs, 4))) return HUBKV_EALIGN;
+  if ((evicted && !aligned(evicted, 4)) || (probs && !aligned(probs, 4)) ||
+      (out && !aligned(out, 4)))
+    return HUBKV_EALIGN;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -241,7 +243,7 @@ int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, voi
   a.include_self = include_self ? 1 : 0;
   a.scale = scale;
   return hip_status(launch_h2o_step(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, a, evicted,
-                                    probs, (hipStream_t)stream));
+                                    probs, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

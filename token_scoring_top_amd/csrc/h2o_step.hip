@@ -12,8 +12,17 @@
 // lanes per slot row: each lane loads 16 bytes of the row and the partial dot
 // products are folded with shuffles; the logits of the group's query heads
 // stay in LDS.  After block-wide softmax statistics, each thread updates the
-// scores of the slots it owns and tracks the eviction candidate with the
-// smallest (score, position); a block reduction picks the slot to overwrite.
+// scores of the slots it owns (the probabilities replace the logits in LDS)
+// and tracks the eviction candidate with the smallest (score, position); a
+// block reduction picks the slot to overwrite.
+//
+// Optional attention output (KV-cache page, section 1.1, decode attention;
+// H2O page, problem statement: only retained tokens enter the normaliser): a
+// second sweep reads the V rows of the occupied slots once and accumulates
+// sum_slot p_h(slot) v_slot per query head, each lane owning a few columns;
+// the partial sums are folded across the lanes of a wave with shuffles and
+// across waves in LDS, in a fixed order.  The sweep reads the cache before the
+// new token's row is written into its slot.
 #include "internal.hpp"
 
 namespace hubkv {
@@ -21,8 +30,18 @@ namespace hubkv {
 namespace {
 
 constexpr int kH2OThreads = 512;
-constexpr int kMaxG = 16;
+constexpr int kH2OWaves = kH2OThreads / 64;
 constexpr float kLog2eH = 1.4426950408889634f;
+
+// a lane's piece of a row: W 32-bit words
+template <int W>
+struct Words {
+  typedef uint32_t __attribute__((ext_vector_type(W))) type;
+};
+template <>
+struct Words<1> {
+  typedef uint32_t type;
+};
 
 template <typename T>
 __device__ __forceinline__ float to_f(T x);
@@ -39,21 +58,26 @@ __device__ __forceinline__ uint32_t asc_key(float v) {
 
 __device__ __forceinline__ int G_of(const H2OArgs& a) { return a.Hq / a.Hkv; }
 
-template <typename T, int D>
+// KG: the group size G rounded up to a power of two (register arrays and
+// unrolled head loops are sized by it; heads h >= G are skipped).
+template <typename T, int D, int KG>
 __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ k_cache, T* __restrict__ v_cache, float* __restrict__ acc,
     int32_t* __restrict__ pos, H2OArgs a, int32_t* __restrict__ evicted,
-    float* __restrict__ probs) {
+    float* __restrict__ probs, float* __restrict__ out) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane piece
   constexpr int LPR = D / EPL;              // lanes per slot row
   constexpr int RPW = 64 / LPR;             // rows per wave per sweep step
-  constexpr int WAVES = kH2OThreads / 64;
-  extern __shared__ float lg[];  // [G][C] logits in log2 units, then [C] positions
+  constexpr int WAVES = kH2OWaves;
+  // dynamic LDS: [G][C] logits in log2 units (then probabilities), [C] slot
+  // positions, and with an output [WAVES][G][D] per-wave partial sums
+  extern __shared__ float lg[];
   int32_t* pl = (int32_t*)(lg + G_of(a) * a.C);
-  __shared__ float qs[kMaxG][D];
-  __shared__ float red[WAVES][kMaxG], red2[WAVES][kMaxG];
-  __shared__ float Mh[kMaxG], iLh[kMaxG], selfx[kMaxG];
+  float* part = (float*)(pl + a.C);
+  __shared__ float qs[KG][D];
+  __shared__ float red[WAVES][KG], red2[WAVES][KG];
+  __shared__ float Mh[KG], iLh[KG], selfx[KG], pself[KG];
   __shared__ unsigned long long cand_key[WAVES];
   __shared__ int cand_slot[WAVES], empty_w[WAVES];
   __shared__ int dec_slot;
@@ -76,9 +100,9 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   const int32_t* P = pos + (int64_t)u * C;
   float* A = acc + (int64_t)u * C;
   const int piece = lane % LPR, rsub = lane / LPR;
-  float om[kMaxG], os[kMaxG];
+  float om[KG], os[KG];
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < KG; ++h) {
     om[h] = -INFINITY;
     os[h] = 0.f;
   }
@@ -113,7 +137,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       for (int x = 0; x < EPL; ++x) kv[x] = to_f<T>(e[x]);
       const bool occ = j < C && pl[j] >= 0;
 #pragma unroll
-      for (int h = 0; h < kMaxG; ++h) {
+      for (int h = 0; h < KG; ++h) {
         if (h >= G) break;
         float d = 0.f;
 #pragma unroll
@@ -147,7 +171,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
 
   // ---- softmax statistics per query head: merge the lanes' running (m, s)
 #pragma unroll
-  for (int h = 0; h < kMaxG; ++h) {
+  for (int h = 0; h < KG; ++h) {
     if (h >= G) break;
     float m = om[h], sm = os[h];
 #pragma unroll
@@ -178,6 +202,28 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   }
   __syncthreads();
 
+  // ---- value sweep geometry: a lane owns EPLV columns of a V row, sized so
+  // the KG x EPLV running sums stay within 32 registers
+  constexpr int EPLV = sizeof(T) == 2 ? (KG <= 4 ? 8 : 32 / KG) : (KG <= 8 ? 4 : 2);
+  constexpr int WV = EPLV * (int)sizeof(T) / 4;  // 32-bit words per lane piece
+  constexpr int LPRV = D / EPLV;                 // lanes per V row
+  constexpr int RPWV = 64 / LPRV;                // V rows per wave per step
+  constexpr int kStepV = WAVES * RPWV * kUnroll;
+  typedef typename Words<WV>::type VW;
+  const T* Vc = v_cache + (int64_t)u * C * D;
+  const int pv = lane % LPRV, rv = lane / LPRV;
+  auto load_v = [&](int j0, VW (&dst)[kUnroll]) {
+#pragma unroll
+    for (int uu = 0; uu < kUnroll; ++uu) {
+      const int j = j0 + uu * WAVES * RPWV + rv;
+      const int jc = j < C ? j : C - 1;
+      dst[uu] = *(const VW*)(Vc + (int64_t)jc * D + pv * EPLV);
+    }
+  };
+  VW vnx[kUnroll];
+  // the first V rows are in flight during the score update
+  if (out) load_v(wave * RPWV, vnx);
+
   // ---- score update, eviction candidate, first empty slot
   const int64_t lo = a.n_sink, hi = t - a.n_recent;
   unsigned long long best = ~0ull;
@@ -188,6 +234,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     for (int h = 0; h < G; ++h) {
       const float p = pj >= 0 ? __builtin_amdgcn_exp2f(lg[h * C + j] - Mh[h]) * iLh[h] : 0.f;
       add += p;
+      lg[h * C + j] = p;
       if (probs) probs[((int64_t)b * a.Hq + g * G + h) * (C + 1) + j] = p;
     }
     if (pj < 0) {
@@ -226,6 +273,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       const float p = (Mh[h] > -INFINITY && selfx[h] > -INFINITY)
                           ? __builtin_amdgcn_exp2f(selfx[h] - Mh[h]) * iLh[h] : 0.f;
       self_acc += p;
+      pself[h] = p;
       if (probs) probs[((int64_t)b * a.Hq + g * G + h) * (C + 1) + C] = p;
     }
     unsigned long long bk = ~0ull;
@@ -261,6 +309,61 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     if (evicted) evicted[u] = ev;
   }
   __syncthreads();
+
+  // ---- attention output: sum over occupied slots of p_h(slot) * v_slot
+  if (out) {
+    float o[KG][EPLV];
+#pragma unroll
+    for (int h = 0; h < KG; ++h)
+#pragma unroll
+      for (int x = 0; x < EPLV; ++x) o[h][x] = 0.f;
+    for (int j0 = wave * RPWV; j0 < C; j0 += kStepV) {
+      VW raw[kUnroll];
+#pragma unroll
+      for (int uu = 0; uu < kUnroll; ++uu) raw[uu] = vnx[uu];
+      if (j0 + kStepV < C) load_v(j0 + kStepV, vnx);
+#pragma unroll
+      for (int uu = 0; uu < kUnroll; ++uu) {
+        const int j = j0 + uu * WAVES * RPWV + rv;
+        // empty slots hold no token, and their rows may hold anything
+        if (j < C && pl[j] >= 0) {
+          const T* e = (const T*)&raw[uu];
+          float vv[EPLV];
+#pragma unroll
+          for (int x = 0; x < EPLV; ++x) vv[x] = to_f<T>(e[x]);
+#pragma unroll
+          for (int h = 0; h < KG; ++h) {
+            if (h >= G) break;
+            const float p = lg[h * C + j];
+#pragma unroll
+            for (int x = 0; x < EPLV; ++x) o[h][x] = fmaf(p, vv[x], o[h][x]);
+          }
+        }
+      }
+    }
+    // fold the rows of a wave, then park the wave's sums in LDS
+#pragma unroll
+    for (int h = 0; h < KG; ++h) {
+      if (h >= G) break;
+#pragma unroll
+      for (int x = 0; x < EPLV; ++x) {
+        float v = o[h][x];
+#pragma unroll
+        for (int off = LPRV; off < 64; off <<= 1) v += __shfl_xor(v, off);
+        if (rv == 0) part[(wave * G + h) * D + pv * EPLV + x] = v;
+      }
+    }
+    __syncthreads();  // every wave's V reads are done before the slot rewrite below
+    const T* vn = v_new + ((int64_t)b * a.Hkv + g) * D;
+    for (int i = tid; i < G * D; i += kH2OThreads) {
+      const int h = i / D, e = i % D;
+      float v = 0.f;
+      for (int w = 0; w < WAVES; ++w) v += part[(w * G + h) * D + e];
+      v = fmaf(pself[h], to_f<T>(vn[e]), v);
+      out[((int64_t)b * a.Hq + g * G + h) * D + e] = v;
+    }
+  }
+
   const int slot = dec_slot;
   if (slot >= 0) {
     // the slot's owner thread rewrites its score and position (it wrote the
@@ -280,24 +383,53 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
 
 }  // namespace
 
-size_t h2o_lds_bytes(int G, int C) { return (size_t)G * C * sizeof(float) + (size_t)C * sizeof(int32_t); }
+size_t h2o_lds_bytes(int G, int C, int d, bool with_out) {
+  return (size_t)G * C * sizeof(float) + (size_t)C * sizeof(int32_t) +
+         (with_out ? (size_t)kH2OWaves * G * d * sizeof(float) : 0);
+}
+
+namespace {
+
+template <typename T, int D>
+void launch_h2o_t(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                  void* v_cache, float* acc, int32_t* pos, const H2OArgs& a, int32_t* evicted,
+                  float* probs, float* out, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const size_t lds = h2o_lds_bytes(G, a.C, D, out != nullptr);
+  const dim3 grid(a.B * a.Hkv), block(kH2OThreads);
+#define H2O_LAUNCH(KG)                                                                          \
+  hipLaunchKernelGGL((h2o_step_kernel<T, D, KG>), grid, block, lds, stream, (const T*)q,        \
+                     (const T*)k_new, (const T*)v_new, (T*)k_cache, (T*)v_cache, acc, pos, a,   \
+                     evicted, probs, out)
+  if (G == 1) H2O_LAUNCH(1);
+  else if (G == 2) H2O_LAUNCH(2);
+  else if (G <= 4) H2O_LAUNCH(4);
+  else if (G <= 8) H2O_LAUNCH(8);
+  else H2O_LAUNCH(16);
+#undef H2O_LAUNCH
+}
+
+}  // namespace
 
 hipError_t launch_h2o_step(const void* q, const void* k_new, const void* v_new, int dtype,
                            void* k_cache, void* v_cache, float* acc, int32_t* pos,
-                           const H2OArgs& a, int32_t* evicted, float* probs, hipStream_t stream) {
-  const int G = a.Hq / a.Hkv;
-  const size_t lds = h2o_lds_bytes(G, a.C);
-  const dim3 grid(a.B * a.Hkv), block(kH2OThreads);
-#define H2O_LAUNCH(T, D)                                                                        \
-  hipLaunchKernelGGL((h2o_step_kernel<T, D>), grid, block, lds, stream, (const T*)q,            \
-                     (const T*)k_new, (const T*)v_new, (T*)k_cache, (T*)v_cache, acc, pos, a,   \
-                     evicted, probs)
+                           const H2OArgs& a, int32_t* evicted, float* probs, float* out,
+                           hipStream_t stream) {
   if (dtype == 1) {
-    if (a.d == 128) H2O_LAUNCH(__bf16, 128); else H2O_LAUNCH(__bf16, 64);
+    if (a.d == 128)
+      launch_h2o_t<__bf16, 128>(q, k_new, v_new, k_cache, v_cache, acc, pos, a, evicted, probs,
+                                out, stream);
+    else
+      launch_h2o_t<__bf16, 64>(q, k_new, v_new, k_cache, v_cache, acc, pos, a, evicted, probs,
+                               out, stream);
   } else {
-    if (a.d == 128) H2O_LAUNCH(float, 128); else H2O_LAUNCH(float, 64);
+    if (a.d == 128)
+      launch_h2o_t<float, 128>(q, k_new, v_new, k_cache, v_cache, acc, pos, a, evicted, probs,
+                               out, stream);
+    else
+      launch_h2o_t<float, 64>(q, k_new, v_new, k_cache, v_cache, acc, pos, a, evicted, probs,
+                              out, stream);
   }
-#undef H2O_LAUNCH
   return hipGetLastError();
 }
 

@@ -98,6 +98,7 @@ struct H2OArgs {
 
 hipError_t launch_h2o_step(const void* q, const void* k_new, const void* v_new, int dtype,
                            void* k_cache, void* v_cache, float* acc, int32_t* pos,
-                           const H2OArgs& a, int32_t* evicted, float* probs, hipStream_t stream);
+                           const H2OArgs& a, int32_t* evicted, float* probs, float* out,
+                           hipStream_t stream);
 
 }  // namespace hubkv
