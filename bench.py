@@ -232,6 +232,57 @@ def bench_decode(args, w):
     return 0
 
 
+def bench_coverage(args):
+    """Cluster-coverage diagnostic: on workloads with planted key bursts, the
+    number of bursts that keep at least one token, for a plain Top-K (r = 0,
+    so z = s) and for the hub-corrected score under two readings of r (r =
+    kept fraction, and r = 1 - kept fraction), across budgets.  One JSON line
+    per workload; the path (score, refine, select) runs on the GPU."""
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    import token_scoring_top_amd as hk
+    from token_scoring_top_amd.diagnostics import cluster_coverage, tokens_in_clusters
+
+    budgets = [0.01, 0.02, 0.05, 0.1, 0.2]
+    for wid in (2, 6):
+        w = S.workload(wid)
+        q, k, _ = S.prefill_layer_inputs(w, 0, with_v=False, threads=min(16, _cores()))
+
+        def dev(x):
+            bits = S.to_bf16_bits(x).view(np.int16)
+            return torch.from_numpy(np.ascontiguousarray(bits)).cuda().view(torch.bfloat16)
+
+        Qd, Kd = dev(q[None]), dev(k[None])
+        del q, k
+        spans = S.cluster_spans(w, 0)
+        ncl = sum(len(sp) for sp in spans)
+        ntok = sum(e - s for sp in spans for s, e in sp)
+        s, st = hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal)
+        rows = []
+        for bud in budgets:
+            kept = S.budgets(w.seqlens, bud)
+            row = {"budget": bud, "kept_per_head": int(kept.sum())}
+            for name, r in (("plain_topk", 0.0), ("r=budget", bud), ("r=1-budget", 1.0 - bud)):
+                z, _ = hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                                       beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=r)
+                idx = hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent)
+                ih = idx.cpu().numpy()
+                cov = cluster_coverage(ih, kept, spans).sum(axis=2)      # [L][Hkv]
+                tin = tokens_in_clusters(ih, kept, spans).sum(axis=2)
+                row[name] = {"covered_mean": float(cov.mean()), "covered_min": int(cov.min()),
+                             "covered_max": int(cov.max()),
+                             "tokens_in_bursts_mean": float(tin.mean())}
+            rows.append(row)
+        print(json.dumps({"diagnostic": "planted-burst coverage", "workload": w.name,
+                          "bursts": ncl, "burst_tokens": ntok, "heads": w.Hkv,
+                          "r_readings": {"plain_topk": 0.0, "r=budget": "budget",
+                                         "r=1-budget": "1 - budget"},
+                          "rows": rows}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +293,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--coverage", action="store_true",
+                    help="planted-burst coverage diagnostic instead of the benchmark")
     ap.add_argument("--attn-out", action="store_true",
                     help="decode workload: h2o_step also writes the attention output")
     args = ap.parse_args(argv)
@@ -264,6 +317,8 @@ def main(argv=None):
     hk.lib()  # fails loudly when the native library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.coverage:
+        return bench_coverage(args)
     w = S.workload(args.workload)
     if isinstance(w, S.DecodeWorkload):
         return bench_decode(args, w)

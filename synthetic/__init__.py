@@ -34,7 +34,7 @@ __all__ = [
     "PrefillWorkload", "DecodeWorkload", "WORKLOADS", "workload",
     "to_bf16_bits", "bf16_bits_to_f32", "round_bf16",
     "prefill_inputs", "prefill_layer_inputs", "random_scores",
-    "decode_unit_stream", "decode_random_state", "budgets",
+    "decode_unit_stream", "decode_random_state", "budgets", "cluster_spans",
 ]
 
 
@@ -79,6 +79,7 @@ class PrefillWorkload:
     dtype: str                      # "f32" or "bf16"
     clusters: Optional[tuple]       # per sequence: number of planted key bursts
     cluster_len: tuple = (16, 16)   # inclusive range of burst lengths
+    cluster_gain: tuple = (3.0, 3.0)  # range of a burst's key gain along the window-query mean
     zipf_alpha: Optional[float] = None
     budget: float = 0.1
     r: float = 0.1
@@ -163,6 +164,12 @@ WORKLOADS = {
     # H2O streaming decode
     4: DecodeWorkload(4, "h2o-decode-b16-h32-d128-bf16-c4096", 16, 32, 32, 128,
                       heavy=2048, recent=2048, prompt=16384, decode=512, dtype="bf16"),
+    # coverage diagnostic: bursts of graded strength (key gain 4..24 along the
+    # window-query mean), so a plain Top-K can spend its budget inside the
+    # strongest bursts
+    6: PrefillWorkload(6, "coverage-graded-n32768-h8-d128-bf16", (32768,), 1, 8, 8, 128, 64,
+                       "bf16", clusters=(256,), cluster_len=(8, 64), cluster_gain=(4.0, 24.0),
+                       budget=0.02, r=0.02, n_sink=4, n_recent=64),
     # ragged batch at scale: 4 sequences 64K..512K, 8 KV heads x 4, window 128
     5: PrefillWorkload(5, "ragged-b4-64k-512k-hkv8-g4-d128-bf16", (65536, 131072, 262144, 524288),
                        1, 32, 8, 128, 128, "bf16",
@@ -211,6 +218,31 @@ def _cluster_spans(rng, n_clusters, lens_range, lo, hi):
     return spans
 
 
+def _spans_and_gains(w: PrefillWorkload, layer: int):
+    seed = 1000 * w.wid + layer
+    base = np.random.default_rng(seed)
+    spans, gains = [], []
+    for b, n in enumerate(w.seqlens):
+        if w.clusters is not None:
+            sp = _cluster_spans(base, w.clusters[b], w.cluster_len, w.n_sink, n - w.n_recent)
+        else:
+            sp = []
+        spans.append(sp)
+        lo, hi = w.cluster_gain
+        if lo == hi:
+            gains.append(None)
+        else:
+            grng = np.random.default_rng([seed, 1, b])
+            gains.append(grng.uniform(lo, hi, size=len(sp)).astype(np.float32))
+    return spans, gains
+
+
+def cluster_spans(w: PrefillWorkload, layer: int = 0):
+    """The planted bursts of one layer: per sequence, a list of [start, end)
+    positions local to the sequence (the same spans prefill_layer_inputs plants)."""
+    return _spans_and_gains(w, layer)[0]
+
+
 def prefill_layer_inputs(w: PrefillWorkload, layer: int = 0, with_v: bool = True, threads: int = 8):
     """One layer of Q [Hq][B*W][d], K [Hkv][T][d], V [Hkv][T][d] as float32
     (bf16-representable when w.dtype == 'bf16').  Seed = 1000*wid + layer; one
@@ -221,15 +253,8 @@ def prefill_layer_inputs(w: PrefillWorkload, layer: int = 0, with_v: bool = True
     Q = np.empty((w.Hq, B * W, d), np.float32)
     K = np.empty((w.Hkv, T, d), np.float32)
     V = np.empty((w.Hkv, T, d), np.float32) if with_v else None
-    base = np.random.default_rng(seed)
-    # burst spans shared by every head of a sequence
-    spans = []
-    for b, n in enumerate(w.seqlens):
-        if w.clusters is not None:
-            spans.append(_cluster_spans(base, w.clusters[b], w.cluster_len,
-                                        w.n_sink, n - w.n_recent))
-        else:
-            spans.append([])
+    # burst spans (and gains) shared by every head of a sequence
+    spans, gains = _spans_and_gains(w, layer)
     unit_rngs = _streams(seed, w.Hkv)
 
     def unit(g):
@@ -248,9 +273,11 @@ def prefill_layer_inputs(w: PrefillWorkload, layer: int = 0, with_v: bool = True
         for b, sp in enumerate(spans):
             if not sp:
                 continue
-            center = 3.0 * q[:, b * W:(b + 1) * W, :].reshape(-1, d).mean(axis=0)
-            for (s0, s1) in sp:
-                k[cu[b] + s0:cu[b] + s1] = center[None, :] + _normal(rng, (s1 - s0, d), 0.3)
+            mean = q[:, b * W:(b + 1) * W, :].reshape(-1, d).mean(axis=0)
+            center = np.float32(w.cluster_gain[0]) * mean if gains[b] is None else None
+            for j, (s0, s1) in enumerate(sp):
+                cj = center if gains[b] is None else gains[b][j] * mean
+                k[cu[b] + s0:cu[b] + s1] = cj[None, :] + _normal(rng, (s1 - s0, d), 0.3)
         if w.dtype == "bf16":
             q = round_bf16(q)
             k = round_bf16(k)
