@@ -59,6 +59,10 @@ def lib():
         L.orc_protected_count.restype = C.c_int64
         L.orc_select.argtypes = [_f32p, C.c_int, _i64p, C.c_int, C.c_int, _i64p, C.c_int, C.c_int,
                                  _i32p]
+        L.orc_select_layer.argtypes = [_f32p, C.c_int, _i64p, C.c_int, C.c_int, _i64p, C.c_int,
+                                       C.c_int, C.c_int, _i32p, _i32p]
+        L.orc_compact_layer.argtypes = [C.c_void_p, C.c_void_p, _i32p, _i32p, C.c_int, C.c_int,
+                                        _i64p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.orc_compact.argtypes = [C.c_void_p, C.c_void_p, _i32p, C.c_int, C.c_int, _i64p, _i64p,
                                   C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.orc_h2o_step.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _i32p, _i64p, C.c_int,
@@ -138,6 +142,39 @@ def select(z, seqlens, kept, n_sink, n_recent):
     idx = np.zeros((L, Hkv, int(kp.sum())), np.int32)
     _check(lib().orc_select(z, sl.size, sl, L, Hkv, kp, int(n_sink), int(n_recent), idx))
     return idx
+
+
+def select_layer(z, seqlens, layer_kept, n_sink, n_recent, floor_min):
+    """Layer-wide budget: z [L][Hkv][T], layer_kept [L][B] (kept total over the
+    layer's heads per sequence).  Returns (idx [sum layer_kept], head_kept
+    [L][B][Hkv]); idx holds, per (layer, sequence), the heads' ascending
+    positions one head after the other."""
+    z = _c(z, np.float32)
+    L, Hkv, T = z.shape
+    sl = _c(seqlens, np.int64)
+    lk = _c(np.asarray(layer_kept, np.int64).reshape(L, sl.size), np.int64)
+    idx = np.zeros(int(lk.sum()), np.int32)
+    hk = np.zeros((L, sl.size, Hkv), np.int32)
+    _check(lib().orc_select_layer(z, sl.size, sl, L, Hkv, lk, int(n_sink), int(n_recent),
+                                  int(floor_min), idx, hk))
+    return idx, hk
+
+
+def compact_layer(k_in, v_in, idx, head_kept, seqlens):
+    """Rows of a layer-wide selection: k_in/v_in [L][Hkv][T][d] (bit copy) ->
+    [sum of kept][d]."""
+    k_in = np.ascontiguousarray(k_in)
+    v_in = np.ascontiguousarray(v_in)
+    L, Hkv, T, d = k_in.shape
+    hk = _c(head_kept, np.int32)
+    K = int(hk.sum())
+    ko = np.empty((K, d), k_in.dtype)
+    vo = np.empty((K, d), v_in.dtype)
+    sl = _c(seqlens, np.int64)
+    _check(lib().orc_compact_layer(k_in.ctypes.data, v_in.ctypes.data, _c(idx, np.int32), hk,
+                                   k_in.dtype.itemsize, sl.size, sl, L, Hkv, d, ko.ctypes.data,
+                                   vo.ctypes.data))
+    return ko, vo
 
 
 def compact(k_in, v_in, idx, seqlens, kept):

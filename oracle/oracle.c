@@ -40,7 +40,12 @@
  *       is over capacity the lowest accumulated score among tokens outside
  *       the sink and recent windows is evicted, ties to the oldest position;
  *   R11 the H2O step's attention output uses those same probabilities on the
- *       values of the same tokens (before the new token is inserted).
+ *       values of the same tokens (before the new token is inserted);
+ *   R12 layer-wide budget: the caller gives the kept total of a (layer,
+ *       sequence) over all its KV heads; each head first keeps its protected
+ *       positions and a floor of its own best candidates, and the rest of
+ *       the total goes to the best remaining (head, position) pairs, ties to
+ *       the lower head, then the lower position.
  */
 #include <math.h>
 #include <stdint.h>
@@ -338,6 +343,111 @@ int orc_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv, co
 }
 
 /* --------------------------------------------------------------------------
+ * Layer-wide budget (NestedKV summary page, head-wise memory allocation: the
+ * layer's budget goes to the globally highest (token, head) pairs, each head
+ * keeping a minimum of its own; KV-cache survey page, section 4.4: budgets
+ * set per layer).  Reading R12.  Per (layer l, sequence b):
+ *   every head keeps the protected positions and its floor: the first
+ *   f = min(floor_min, number of candidates) of its candidates in the order
+ *   of reading R9 (z descending, position ascending, NaN lowest);
+ *   the other candidates of all heads compete for the rest of the budget,
+ *   R = layer_kept[l][b] - Hkv * (|P| + f), in (z descending, head
+ *   ascending, position ascending) order.
+ * z [L][Hkv][T]; layer_kept [L][B] host.  idx: for each (l, b) in row-major
+ * order, the heads' kept positions head after head, each ascending;
+ * head_kept [L][B][Hkv].
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float z;
+  int64_t pos;
+  int head;
+} zhp_t;
+
+static int zhp_cmp(const void* a, const void* b) {
+  const zhp_t* x = (const zhp_t*)a;
+  const zhp_t* y = (const zhp_t*)b;
+  const int xn = isnan(x->z), yn = isnan(y->z);
+  if (xn != yn) return xn ? 1 : -1;
+  if (!xn) {
+    if (x->z > y->z) return -1;
+    if (x->z < y->z) return 1;
+  }
+  if (x->head != y->head) return x->head < y->head ? -1 : 1;
+  return (x->pos < y->pos) ? -1 : (x->pos > y->pos ? 1 : 0);
+}
+
+int orc_select_layer(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
+                     const int64_t* layer_kept, int n_sink, int n_recent, int floor_min,
+                     int32_t* idx, int32_t* head_kept) {
+  if (n_sink < 0 || n_recent < 0 || floor_min < 0 || Hkv < 1) return ORC_EINVAL;
+  for (int l = 0; l < L; ++l)
+    for (int b = 0; b < B; ++b) {
+      const int64_t N = seqlens[b];
+      const int64_t P = orc_protected_count(N, n_sink, n_recent);
+      const int64_t f = floor_min < N - P ? floor_min : N - P;
+      const int64_t k = layer_kept[(int64_t)l * B + b];
+      if (k < (int64_t)Hkv * (P + f) || k > (int64_t)Hkv * N) return ORC_EINVAL;
+    }
+  const int64_t T = total_len(B, seqlens);
+  const int units = L * B;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int u = 0; u < units; ++u) {
+    const int l = u / B, b = u % B;
+    const int64_t N = seqlens[b];
+    const int64_t P = orc_protected_count(N, n_sink, n_recent);
+    const int64_t f = floor_min < N - P ? floor_min : N - P;
+    int64_t off = 0;
+    for (int v = 0; v < u; ++v) off += layer_kept[v];
+    unsigned char* keep = (unsigned char*)calloc((size_t)(Hkv * N), 1);
+    zpos_t* cand = (zpos_t*)malloc((size_t)N * sizeof(zpos_t));
+    zhp_t* pool = (zhp_t*)malloc((size_t)(Hkv * N) * sizeof(zhp_t));
+    int64_t np = 0;
+    for (int g = 0; g < Hkv; ++g) {
+      const float* zb = z + (int64_t)(l * Hkv + g) * T + seq_start(b, seqlens);
+      unsigned char* kg = keep + (int64_t)g * N;
+      int64_t nc = 0;
+      for (int64_t i = 0; i < N; ++i) {
+        if ((i < n_sink) || (i >= N - n_recent)) {
+          kg[i] = 1;
+        } else {
+          cand[nc].z = zb[i];
+          cand[nc].pos = i;
+          ++nc;
+        }
+      }
+      qsort(cand, (size_t)nc, sizeof(zpos_t), zpos_cmp);
+      for (int64_t j = 0; j < nc; ++j) {
+        if (j < f) {
+          kg[cand[j].pos] = 1; /* the head's floor */
+        } else {
+          pool[np].z = cand[j].z;
+          pool[np].pos = cand[j].pos;
+          pool[np].head = g;
+          ++np;
+        }
+      }
+    }
+    qsort(pool, (size_t)np, sizeof(zhp_t), zhp_cmp);
+    const int64_t R = layer_kept[u] - (int64_t)Hkv * (P + f);
+    for (int64_t j = 0; j < R; ++j) keep[(int64_t)pool[j].head * N + pool[j].pos] = 1;
+    int64_t o = off;
+    for (int g = 0; g < Hkv; ++g) {
+      int32_t n = 0;
+      for (int64_t i = 0; i < N; ++i)
+        if (keep[(int64_t)g * N + i]) {
+          idx[o++] = (int32_t)i;
+          ++n;
+        }
+      head_kept[(int64_t)u * Hkv + g] = n;
+    }
+    free(keep);
+    free(cand);
+    free(pool);
+  }
+  return ORC_OK;
+}
+
+/* --------------------------------------------------------------------------
  * Compaction: physically drop evicted K/V rows (H2O breakdown page, "two code
  * bases": the real-drop variant removes evicted tokens' K/V from the cache).
  * k_in/v_in [L][Hkv][T][d], idx [L][Hkv][sum kept], out [L][Hkv][sum kept][d].
@@ -361,6 +471,30 @@ int orc_compact(const void* k_in, const void* v_in, const int32_t* idx, int elem
           memcpy((char*)v_out + dst * row, (const char*)v_in + src * row, row);
         }
         koff += kept[b];
+      }
+    }
+  return ORC_OK;
+}
+
+/* Compaction of a layer-wide selection: the rows of idx (orc_select_layer's
+ * layout) in order, each from the head that head_kept assigns it to.
+ * k_out/v_out [sum of layer_kept][d]. */
+int orc_compact_layer(const void* k_in, const void* v_in, const int32_t* idx,
+                      const int32_t* head_kept, int elem_bytes, int B, const int64_t* seqlens,
+                      int L, int Hkv, int d, void* k_out, void* v_out) {
+  const int64_t T = total_len(B, seqlens);
+  const size_t row = (size_t)d * (size_t)elem_bytes;
+  int64_t o = 0;
+  for (int l = 0; l < L; ++l)
+    for (int b = 0; b < B; ++b) {
+      const int64_t cu = seq_start(b, seqlens);
+      for (int g = 0; g < Hkv; ++g) {
+        const int32_t n = head_kept[((int64_t)l * B + b) * Hkv + g];
+        for (int32_t j = 0; j < n; ++j, ++o) {
+          const int64_t src = (int64_t)(l * Hkv + g) * T + cu + idx[o];
+          memcpy((char*)k_out + o * row, (const char*)k_in + src * row, row);
+          memcpy((char*)v_out + o * row, (const char*)v_in + src * row, row);
+        }
       }
     }
   return ORC_OK;

@@ -15,7 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_score.py", "tests/test_oracle_refine.py",
-        "tests/test_oracle_select.py", "tests/test_oracle_h2o.py"]
+        "tests/test_oracle_select.py", "tests/test_oracle_h2o.py",
+        "tests/test_oracle_select_layer.py"]
 
 MUTANTS = {
     "causal-off-by-one": ("const int64_t nvis = causal ? p + 1 : N;",
@@ -52,6 +53,15 @@ MUTANTS = {
                              "o += exp(x[j] - m) * (double)V[(int64_t)j * d + e];"),
     "h2o-out-empty-slots-included": ("if (P[j] >= 0) o += exp(x[j] - m)",
                                      "o += exp(x[j] - m)"),
+    "layer-tie-to-higher-head": ("if (x->head != y->head) return x->head < y->head ? -1 : 1;",
+                                 "if (x->head != y->head) return x->head > y->head ? -1 : 1;"),
+    "layer-floor-off-by-one": ("if (j < f) {\n          kg[cand[j].pos] = 1; /* the head's floor */",
+                               "if (j <= f) {\n          kg[cand[j].pos] = 1; /* the head's floor */"),
+    "layer-pool-ascending": ("    if (x->z > y->z) return -1;\n    if (x->z < y->z) return 1;\n  }\n  if (x->head",
+                             "    if (x->z < y->z) return -1;\n    if (x->z > y->z) return 1;\n  }\n  if (x->head"),
+    "layer-no-floor": ("kg[cand[j].pos] = 1; /* the head's floor */", "(void)0;"),
+    "layer-compact-wrong-head": ("const int64_t src = (int64_t)(l * Hkv + g) * T + cu + idx[o];",
+                                 "const int64_t src = (int64_t)(l * Hkv + (g + 1) % Hkv) * T + cu + idx[o];"),
     "h2o-no-acc-update": ("if (P[j] >= 0) A[j] = (float)((double)A[j] + add[j]);",
                           "if (P[j] >= 0) A[j] = A[j];"),
 }
