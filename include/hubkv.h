@@ -7,6 +7,8 @@
  *   hubkv_refine   HubKV refinement of those scores before Top-K
  *   hubkv_select   per-head Top-K with protected sink and recent tokens
  *   hubkv_compact  gather of the kept K/V rows into a packed cache
+ *   hubkv_select_layer / hubkv_compact_layer
+ *                  a layer's budget shared by its KV heads (per-head floors)
  *   h2o_step       one streaming (decode) step of H2O greedy eviction
  *
  * Conventions shared by every call
@@ -153,6 +155,50 @@ int hubkv_select(const float* z, int B, const int64_t* seqlens /* host */, int L
 int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
                   const int64_t* seqlens /* host */, const int64_t* kept /* host [B] */, int L,
                   int Hkv, int d, void* k_out, void* v_out, void* stream);
+
+/*
+ * hubkv_select_layer -- one budget per (layer, sequence), shared by its KV
+ * heads.
+ *
+ * NestedKV summary page, head-wise memory allocation: the layer's budget goes
+ * to the (token, head) pairs with the highest scores across the layer, every
+ * head keeping a minimum of its own; KV-cache survey page, section 4.4
+ * (PyramidKV): the budget is set per layer, here by the caller.  For each
+ * (layer l, sequence b), with P_b the protected positions (as hubkv_select)
+ * and f_b = min(floor_min, N_b - |P_b|):
+ *   every KV head keeps P_b and its f_b best unprotected positions (z
+ *   descending, position ascending, NaN lowest, -0 == +0);
+ *   the other unprotected (head, position) pairs of the layer compete for
+ *   layer_kept[l][b] - Hkv (|P_b| + f_b) places in (z descending, head
+ *   ascending, position ascending) order.
+ * Each head thus keeps its own top head_kept[l][b][h] positions.
+ * z fp32 [L][Hkv][T].  layer_kept host [L][B], row-major, with
+ * Hkv (|P_b| + f_b) <= layer_kept[l][b] <= Hkv N_b, L * B <= 256, and the sum
+ * over all (l, b) below 2^31.  Outputs: head_kept int32 [L][B][Hkv]; idx
+ * int32 [sum of layer_kept]: for each (l, b) in row-major order (offset =
+ * sum of the earlier layer_kept), the heads' kept positions head after head,
+ * each head's ascending.  workspace >= hubkv_select_layer_workspace(), 256-B
+ * aligned; it holds the search state and is fully rewritten by every call.
+ * Deterministic.
+ */
+size_t hubkv_select_layer_workspace(int B, const int64_t* seqlens /* host */, int L, int Hkv);
+
+int hubkv_select_layer(const float* z, int B, const int64_t* seqlens /* host */, int L, int Hkv,
+                       const int64_t* layer_kept /* host [L][B] */, int n_sink, int n_recent,
+                       int floor_min, int32_t* idx, int32_t* head_kept, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * hubkv_compact_layer -- the K/V rows of a hubkv_select_layer result, packed
+ * in idx's order: row o of (l, b, h) is K[l][h][cu_b + idx[o]] (same for V),
+ * k_out/v_out [sum of layer_kept][d].  head_kept (device) says which head
+ * each row belongs to; layer_kept (host) must be the one given to
+ * hubkv_select_layer.  Positions outside [0, N_b) are skipped.
+ */
+int hubkv_compact_layer(const void* k_in, const void* v_in, int dtype, const int32_t* idx,
+                        const int32_t* head_kept, int B, const int64_t* seqlens /* host */, int L,
+                        int Hkv, const int64_t* layer_kept /* host [L][B] */, int d, void* k_out,
+                        void* v_out, void* stream);
 
 /*
  * h2o_step -- one decode step of H2O greedy eviction on a fixed-slot cache.

@@ -140,6 +140,40 @@ def test_compact_validation():
     assert call(ko=None) == EALIGN
 
 
+def test_select_layer_validation():
+    L = hk.lib()
+    sl = a64([1000])
+    ws = L.hubkv_select_layer_workspace(1, sl, 2, 4)
+    assert ws > 0
+    assert L.hubkv_select_layer_workspace(1, sl, 300, 4) == 0            # L * B > 256
+
+    def call(lk=(500, 500), Lr=2, Hkv=4, ns=4, nr=16, fl=10, idx=P, wsb=ws, seq=(1000,)):
+        return L.hubkv_select_layer(P, len(seq), a64(list(seq)), Lr, Hkv, a64(list(lk)), ns, nr,
+                                    fl, idx, P, P, wsb, None)
+
+    # per-head floor: 4 heads x (20 protected + 10) = 120 at least, 4000 at most
+    assert call(lk=(119, 500)) == EINVAL
+    assert call(lk=(500, 4001)) == EINVAL
+    assert call(fl=-1) == EINVAL
+    assert call(Lr=300, lk=(500,) * 300) == EINVAL
+    assert call(idx=P + 2, lk=(120, 4000)) == EALIGN
+    assert call(wsb=ws - 1, lk=(120, 4000)) == EWS
+    assert call(idx=None, lk=(120, 4000)) == EALIGN
+
+
+def test_compact_layer_validation():
+    L = hk.lib()
+
+    def call(dt=1, d=128, lk=(300,), Hkv=4, ko=P):
+        return L.hubkv_compact_layer(P, P, dt, P, P, 1, a64([100]), 1, Hkv, a64(list(lk)), d, ko,
+                                     P, None)
+
+    assert call(d=96) == EDTYPE
+    assert call(dt=7) == EDTYPE
+    assert call(lk=(401,)) == EINVAL                                      # above Hkv * N
+    assert call(ko=P + 8) == EALIGN
+
+
 def test_h2o_step_validation():
     L = hk.lib()
 

@@ -11,6 +11,8 @@ Functions (names follow the C ABI):
     hubkv_refine(s, seqlens, ...)                      -> (z, beta)
     hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
     hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
+    hubkv_select_layer(z, seqlens, layer_kept, ...)    -> (idx, head_kept)
+    hubkv_compact_layer(k, v, idx, head_kept, seqlens, layer_kept) -> (k_out, v_out)
     h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, ...) -> evicted
 """
 from __future__ import annotations
@@ -51,6 +53,11 @@ _SIGS = {
                           _vp]),
     "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp]),
     "hubkv_compact": (_i, [_vp, _vp, _i, _vp, _i, _i64p, _i64p, _i, _i, _i, _vp, _vp, _vp]),
+    "hubkv_select_layer_workspace": (_sz, [_i, _i64p, _i, _i]),
+    "hubkv_select_layer": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _i, _vp, _vp, _vp, _sz,
+                                _vp]),
+    "hubkv_compact_layer": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i64p, _i, _i, _i64p, _i, _vp, _vp,
+                                 _vp]),
     "h2o_step": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, _i, _f,
                       _i, _vp, _vp, _vp, _vp]),
     "hubkv_protected_count": (_i64, [_i64, _i, _i]),
@@ -211,6 +218,49 @@ def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], 
                                                 _ptr(idx), len(seqlens), _arr64(seqlens),
                                                 _arr64(kept), L, Hkv, d, _ptr(k_out), _ptr(v_out),
                                                 _stream(stream)))
+    return k_out, v_out
+
+
+def hubkv_select_layer(z, seqlens: Sequence[int], layer_kept, n_sink: int, n_recent: int,
+                       floor_min: int = 0, idx=None, head_kept=None, workspace=None, stream=None):
+    """z fp32 [L][Hkv][T]; layer_kept [L][B] kept totals over each layer's heads ->
+    idx int32 [sum layer_kept] (per (layer, sequence), head after head, each
+    ascending), head_kept int32 [L][B][Hkv]."""
+    torch = _torch()
+    L, Hkv, T = z.shape
+    B = len(seqlens)
+    sl = _arr64(seqlens)
+    lk = [int(x) for row in layer_kept for x in (row if hasattr(row, "__len__") else [row])]
+    if len(lk) != L * B:
+        raise ValueError(f"layer_kept must hold L * B = {L * B} totals")
+    if idx is None:
+        idx = torch.empty(sum(lk), dtype=torch.int32, device=z.device)
+    if head_kept is None:
+        head_kept = torch.empty((L, B, Hkv), dtype=torch.int32, device=z.device)
+    nb = lib().hubkv_select_layer_workspace(B, sl, L, Hkv)
+    if workspace is None:
+        workspace = _workspace(nb, z.device)
+    _check("hubkv_select_layer", lib().hubkv_select_layer(
+        _ptr(z), B, sl, L, Hkv, _arr64(lk), int(n_sink), int(n_recent), int(floor_min),
+        _ptr(idx), _ptr(head_kept), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx, head_kept
+
+
+def hubkv_compact_layer(k_in, v_in, idx, head_kept, seqlens: Sequence[int], layer_kept,
+                        k_out=None, v_out=None, stream=None):
+    """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [sum layer_kept][d] in idx's order."""
+    torch = _torch()
+    L, Hkv, T, d = k_in.shape
+    B = len(seqlens)
+    lk = [int(x) for row in layer_kept for x in (row if hasattr(row, "__len__") else [row])]
+    K = sum(lk)
+    if k_out is None:
+        k_out = torch.empty((K, d), dtype=k_in.dtype, device=k_in.device)
+    if v_out is None:
+        v_out = torch.empty((K, d), dtype=v_in.dtype, device=v_in.device)
+    _check("hubkv_compact_layer", lib().hubkv_compact_layer(
+        _ptr(k_in), _ptr(v_in), _dtype_code(k_in), _ptr(idx), _ptr(head_kept), B,
+        _arr64(seqlens), L, Hkv, _arr64(lk), d, _ptr(k_out), _ptr(v_out), _stream(stream)))
     return k_out, v_out
 
 

@@ -77,6 +77,49 @@ int check_score_shape(int L, int Hq, int Hkv, int W, const SeqTable& st) {
   return HUBKV_OK;
 }
 
+// Fill the layer-wide selection table; validates shapes and budgets.
+int make_lsel(LselArgs& a, int B, const int64_t* seqlens, int L, int Hkv, const int64_t* layer_kept,
+              int n_sink, int n_recent, int floor_min) {
+  if (B < 1 || B > kMaxSeqs || !seqlens || !layer_kept) return HUBKV_EINVAL;
+  if (L < 1 || Hkv < 1 || Hkv > 1024 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if ((int64_t)L * B > kMaxLayerSegs || n_sink < 0 || n_recent < 0 || floor_min < 0)
+    return HUBKV_EINVAL;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.L = L;
+  a.Hkv = Hkv;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  int64_t cu = 0, ch = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = seqlens[b];
+    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    const int64_t P = hubkv_protected_count(n, n_sink, n_recent);
+    a.N[b] = (int32_t)n;
+    a.cu[b] = cu;
+    a.f[b] = (int32_t)(floor_min < n - P ? floor_min : n - P);
+    a.ch_off[b] = (int32_t)ch;
+    cu += n;
+    ch += (n + kLselChunk - 1) / kLselChunk;
+  }
+  if (cu >= ((int64_t)1 << 40) || ch > 65535) return HUBKV_EINVAL;
+  a.ch_off[B] = (int32_t)ch;
+  a.nchunk = (int)ch;
+  a.T = cu;
+  int64_t tot = 0;
+  for (int l = 0; l < L; ++l)
+    for (int b = 0; b < B; ++b) {
+      const int64_t n = a.N[b];
+      const int64_t P = hubkv_protected_count(n, n_sink, n_recent);
+      const int64_t k = layer_kept[(int64_t)l * B + b];
+      if (k < (int64_t)Hkv * (P + a.f[b]) || k > (int64_t)Hkv * n) return HUBKV_EINVAL;
+      a.budget[l * B + b] = (int32_t)(k < kMaxTokens ? k : 0);
+      tot += k;
+      if (tot >= kMaxTokens) return HUBKV_EINVAL;
+    }
+  return HUBKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +250,56 @@ int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* 
     return HUBKV_EALIGN;
   return hip_status(launch_compact(k_in, v_in, dtype == HUBKV_BF16 ? 2 : 4, idx, st, L, Hkv, d,
                                    k_out, v_out, (hipStream_t)stream));
+}
+
+size_t hubkv_select_layer_workspace(int B, const int64_t* seqlens, int L, int Hkv) {
+  if (B < 1 || B > kMaxSeqs || !seqlens || L < 1 || Hkv < 1 || Hkv > 1024) return 0;
+  if ((int64_t)L * B > kMaxLayerSegs || (int64_t)L * Hkv > kMaxGridY) return 0;
+  LselArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.L = L;
+  a.Hkv = Hkv;
+  int64_t ch = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens) return 0;
+    ch += (seqlens[b] + kLselChunk - 1) / kLselChunk;
+  }
+  if (ch > 65535) return 0;
+  a.nchunk = (int)ch;
+  return lsel_geometry(a).bytes;
+}
+
+int hubkv_select_layer(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
+                       const int64_t* layer_kept, int n_sink, int n_recent, int floor_min,
+                       int32_t* idx, int32_t* head_kept, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  LselArgs a;
+  int rc = make_lsel(a, B, seqlens, L, Hkv, layer_kept, n_sink, n_recent, floor_min);
+  if (rc) return rc;
+  if (!z || !idx || !head_kept || !workspace) return HUBKV_EALIGN;
+  if (!aligned(z, 4) || !aligned(idx, 4) || !aligned(head_kept, 4) || !aligned(workspace, 256))
+    return HUBKV_EALIGN;
+  const LselGeom g = lsel_geometry(a);
+  if (workspace_bytes < g.bytes) return HUBKV_EWORKSPACE;
+  return hip_status(launch_select_layer(z, a, g, (char*)workspace, idx, head_kept,
+                                        (hipStream_t)stream));
+}
+
+int hubkv_compact_layer(const void* k_in, const void* v_in, int dtype, const int32_t* idx,
+                        const int32_t* head_kept, int B, const int64_t* seqlens, int L, int Hkv,
+                        const int64_t* layer_kept, int d, void* k_out, void* v_out, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  LselArgs a;
+  // the budgets only set the row offsets here: no floor or window bound applies
+  if ((rc = make_lsel(a, B, seqlens, L, Hkv, layer_kept, 0, 0, 0))) return rc;
+  if (!k_in || !v_in || !k_out || !v_out || !idx || !head_kept) return HUBKV_EALIGN;
+  if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      !aligned(idx, 4) || !aligned(head_kept, 4))
+    return HUBKV_EALIGN;
+  return hip_status(launch_compact_layer(k_in, v_in, dtype == HUBKV_BF16 ? 2 : 4, idx, head_kept,
+                                         a, d, k_out, v_out, (hipStream_t)stream));
 }
 
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,

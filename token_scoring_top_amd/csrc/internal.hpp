@@ -84,6 +84,35 @@ hipError_t launch_refine(const float* s, const SeqTable& st, int L, int Hkv,
 hipError_t launch_select(const float* z, const SeqTable& st, int L, int Hkv, int n_sink,
                          int n_recent, int32_t* idx, hipStream_t stream);
 
+// ---- layer-wide budget --------------------------------------------------------------
+constexpr int kMaxLayerSegs = 256;  // (layer, sequence) pairs per call
+constexpr int kLselChunk = 4096;    // positions per work-group
+
+// Kernel-argument table of a layer-wide selection (no device allocation).
+struct LselArgs {
+  int B, L, Hkv, n_sink, n_recent;
+  int nchunk;                       // chunks of one (layer, head) over all sequences
+  int64_t T;                        // packed tokens
+  int32_t N[kMaxSeqs];
+  int64_t cu[kMaxSeqs];
+  int32_t f[kMaxSeqs];              // per-head floor of each sequence
+  int32_t ch_off[kMaxSeqs + 1];     // first chunk of each sequence
+  int32_t budget[kMaxLayerSegs];    // kept total per (layer, sequence), row-major
+};
+
+struct LselGeom {
+  size_t off_hs, off_ss, off_hh, off_hg, off_ch, off_cg, off_ec, bytes;
+};
+
+LselGeom lsel_geometry(const LselArgs& a);
+
+hipError_t launch_select_layer(const float* z, const LselArgs& a, const LselGeom& g, char* ws,
+                               int32_t* idx, int32_t* head_kept, hipStream_t stream);
+
+hipError_t launch_compact_layer(const void* k_in, const void* v_in, int elem_bytes,
+                                const int32_t* idx, const int32_t* head_kept, const LselArgs& a,
+                                int d, void* k_out, void* v_out, hipStream_t stream);
+
 // ---- compaction ------------------------------------------------------------------
 hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, const int32_t* idx,
                           const SeqTable& st, int L, int Hkv, int d, void* k_out, void* v_out,
