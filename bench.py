@@ -293,6 +293,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--layer-budget", action="store_true",
+                    help="prefill: one budget per layer shared by its KV heads (hubkv_select_layer)")
     ap.add_argument("--coverage", action="store_true",
                     help="planted-burst coverage diagnostic instead of the benchmark")
     ap.add_argument("--attn-out", action="store_true",
@@ -360,6 +362,18 @@ def main(argv=None):
     idx = torch.empty((L, Hkv, Ksum), dtype=torch.int32, device="cuda")
     ko = torch.empty((L, Hkv, Ksum, w.d), dtype=Kd.dtype, device="cuda")
     vo = torch.empty_like(ko)
+    # layer-wide budget: each (layer, sequence) keeps Hkv x kept_b over its
+    # heads, every head at least its protected tokens plus a quarter of its
+    # even share
+    lk = [[w.Hkv * int(kb) for kb in kept] for _ in range(L)]
+    floor = int(min(kept)) // 4
+    if args.layer_budget:
+        idx_l = torch.empty(L * Hkv * Ksum, dtype=torch.int32, device="cuda")
+        hkept = torch.empty((L, w.B, Hkv), dtype=torch.int32, device="cuda")
+        ws_l = torch.empty(hk.lib().hubkv_select_layer_workspace(w.B, hk._arr64(w.seqlens), L, Hkv),
+                           dtype=torch.uint8, device="cuda")
+        ko = ko.view(L * Hkv * Ksum, w.d)
+        vo = vo.view(L * Hkv * Ksum, w.d)
     sl = hk._arr64(w.seqlens)
     ws_s = torch.empty(hk.lib().hubkv_score_workspace(w.B, sl, L, w.Hq, Hkv, w.W, w.d,
                                                       1 if elem == 2 else 0),
@@ -377,9 +391,17 @@ def main(argv=None):
                         beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
                         workspace=ws_r, stream=stream)
         if ev: ev[2].record(stream)
-        hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent, idx=idx, stream=stream)
+        if args.layer_budget:
+            hk.hubkv_select_layer(z, w.seqlens, lk, w.n_sink, w.n_recent, floor, idx=idx_l,
+                                  head_kept=hkept, workspace=ws_l, stream=stream)
+        else:
+            hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent, idx=idx, stream=stream)
         if ev: ev[3].record(stream)
-        hk.hubkv_compact(Kd, Vd, idx, w.seqlens, kept, k_out=ko, v_out=vo, stream=stream)
+        if args.layer_budget:
+            hk.hubkv_compact_layer(Kd, Vd, idx_l, hkept, w.seqlens, lk, k_out=ko, v_out=vo,
+                                   stream=stream)
+        else:
+            hk.hubkv_compact(Kd, Vd, idx, w.seqlens, kept, k_out=ko, v_out=vo, stream=stream)
         if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
@@ -417,8 +439,10 @@ def main(argv=None):
     mfma_util = score_flops(w) / (op_ms["score"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12)
     kernels = {"score": "score_pass_mfma<1> (row partials) + score_pass_mfma<2> (fold, column sums)" if elem == 2 else
                "score_stats_f32 + score_combine + score_probs_f32 + stats_final",
-               "refine": "refine_kernel", "select": "select_kernel",
-               "compact": "compact_kernel"}
+               "refine": "refine_kernel",
+               "select": ("lsel_init + lsel_floor_level<0..2> + lsel_pool_level<0..2> + lsel_count"
+                          " + lsel_emit_count + lsel_emit") if args.layer_budget else "select_kernel",
+               "compact": "compact_layer_kernel" if args.layer_budget else "compact_kernel"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -438,7 +462,16 @@ def main(argv=None):
         q0, k0, v0 = q0[None], k0[None], v0[None]
         reps, tc0 = 0, time.perf_counter()
         while True:
-            oracle.prefill_chain(q0, k0, v0, ws)
+            if args.layer_budget:
+                s0, st0 = oracle.score(q0, k0, ws.seqlens, ws.W, ws.scale, ws.causal)
+                z0 = oracle.refine(s0, ws.seqlens, oracle.beta(st0, ws.seqlens, ws.beta_lo,
+                                                              ws.beta_hi), ws.pool, ws.gamma, ws.r)
+                kb0 = ws.kept()
+                i0, h0 = oracle.select_layer(z0, ws.seqlens, [[ws.Hkv * int(x) for x in kb0]],
+                                             ws.n_sink, ws.n_recent, int(min(kb0)) // 4)
+                oracle.compact_layer(k0, v0, i0, h0, ws.seqlens)
+            else:
+                oracle.prefill_chain(q0, k0, v0, ws)
             reps += 1
             if time.perf_counter() - tc0 >= args.cpu_budget_s or reps >= 50:
                 break
@@ -464,6 +497,8 @@ def main(argv=None):
         "config": {"workload": w.name, "seqlens": list(w.seqlens), "layers": w.L, "Hq": w.Hq,
                    "Hkv": w.Hkv, "d": w.d, "window": w.W, "budget": w.budget, "r": w.r,
                    "n_sink": w.n_sink, "n_recent": w.n_recent, "kept_per_head": int(Ksum),
+                   "budget_scope": "layer" if args.layer_budget else "head",
+                   "head_floor": floor if args.layer_budget else None,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "op": dom,

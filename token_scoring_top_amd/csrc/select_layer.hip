@@ -404,22 +404,39 @@ __global__ __launch_bounds__(kT) void lsel_count(const float* __restrict__ z, Ls
     flag = bump_ag(w.cg + k.s) == (uint32_t)(k.nch * a.Hkv) - 1 ? 1u : 0u;
   }
   __syncthreads();
-  if (!flag || threadIdx.x != 0) return;
-  // the (layer, sequence)'s last work-group, one thread: heads in order
+  if (!flag || wave != 0) return;
+  // the (layer, sequence)'s last work-group, wave 0: heads in groups of 64,
+  // in order, with running totals carried between groups
   const int64_t P = prot_count(k.N, a.n_sink, a.n_recent);
   const int64_t f = a.f[k.b];
-  int64_t off = 0;
-  for (int v = 0; v < k.s; ++v) off += a.budget[v];
-  const int64_t seg_end = off + a.budget[k.s];
-  uint32_t left = ss->rem;
-  for (int hh = 0; hh < a.Hkv; ++hh) {
-    HeadState* o = w.hs + (int64_t)k.s * a.Hkv + hh;
-    const uint32_t ph = o->phi, ct = o->cties, remf = o->remf;
-    uint32_t g2 = ld_ag(&o->gt), e2 = ld_ag(&o->eq);
-    if (ph != kNone && ph > tau) g2 += ct;  // the floor's left-out ties sit above tau
-    if (ph == tau) e2 += ct;
-    const uint32_t x = e2 < left ? e2 : left;
-    left -= x;
+  int64_t seg = 0;
+  for (int v = 0; v < k.s; ++v) seg += a.budget[v];
+  const int64_t seg_end = seg + a.budget[k.s];
+  uint32_t left = ss->rem;   // ties at tau still to hand out
+  int64_t off = seg;         // first row of the group's first head
+  for (int h0 = 0; h0 < a.Hkv; h0 += 64) {
+    const int hh = h0 + lane;
+    const bool on = hh < a.Hkv;
+    HeadState* o = w.hs + (int64_t)k.s * a.Hkv + (on ? hh : 0);
+    uint32_t ph = 0u, ct = 0u, remf = 0u, g2 = 0u, e2 = 0u;
+    if (on) {
+      ph = o->phi;
+      ct = o->cties;
+      remf = o->remf;
+      g2 = ld_ag(&o->gt);
+      e2 = ld_ag(&o->eq);
+      if (ph != kNone && ph > tau) g2 += ct;  // the floor's left-out ties sit above tau
+      if (ph == tau) e2 += ct;
+    }
+    // ties at tau go to the lower heads first: x = clamp(left - ties of the heads before)
+    uint32_t incl = e2;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const uint32_t before = incl - e2;
+    const uint32_t x = before >= left ? 0u : (e2 < left - before ? e2 : left - before);
     uint32_t kap, r;
     if (ph < tau) {
       kap = ph;
@@ -431,16 +448,28 @@ __global__ __launch_bounds__(kT) void lsel_count(const float* __restrict__ z, Ls
       kap = tau;
       r = x;
     }
-    int64_t kh = P + f + g2 + x;
-    if (off + kh > seg_end) kh = seg_end - off;  // never past the (layer, sequence)'s rows
-    o->kappa = kap;
-    o->r = r;
-    o->k = (uint32_t)kh;
-    o->off = off;
-    head_kept[(int64_t)k.s * a.Hkv + hh] = (int32_t)kh;
-    off += kh;
+    const int64_t kh0 = on ? P + f + g2 + x : 0;
+    int64_t kin = kh0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(kin, d);
+      if (lane >= d) kin += y;
+    }
+    const int64_t my_off = off + kin - kh0;
+    int64_t kh = kh0;
+    if (my_off + kh > seg_end) kh = seg_end > my_off ? seg_end - my_off : 0;  // stay in the slice
+    if (on) {
+      o->kappa = kap;
+      o->r = r;
+      o->k = (uint32_t)kh;
+      o->off = my_off;
+      head_kept[(int64_t)k.s * a.Hkv + hh] = (int32_t)kh;
+    }
+    const uint32_t tot_e = __shfl(incl, 63);
+    left = tot_e >= left ? 0u : left - tot_e;
+    off += __shfl(kin, 63);
   }
-  st_ag(w.cg + k.s, 0u);
+  if (lane == 0) st_ag(w.cg + k.s, 0u);
 }
 
 // Keep rule of the emission: protected, above kappa, or one of the first r
@@ -453,11 +482,11 @@ __device__ __forceinline__ void emit_flags(uint32_t x, uint32_t kap, bool& def, 
 // Chunk keys for the emission: protected positions get kNone (kept), positions
 // past the chunk get 0 with `valid` false.
 __device__ __forceinline__ void load_emit(const LselArgs& a, const Chunk& k, int64_t base,
-                                          uint32_t (&key)[16], bool (&valid)[16]) {
+                                          uint32_t (&key)[kPer], bool (&valid)[kPer]) {
   const int64_t lo = a.n_sink, hi = k.N - a.n_recent;
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     const int64_t p = base + 64 * j + lane;
     valid[j] = p < k.p1;
     const float v = k.zb[valid[j] ? p : k.p0];
@@ -473,12 +502,12 @@ __global__ __launch_bounds__(kT) void lsel_emit_count(const float* __restrict__ 
   const Chunk k = chunk_of(a, z);
   const HeadState& hs = w.hs[k.u];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t key[16];
-  bool valid[16];
-  load_emit(a, k, k.p0 + 1024 * wave, key, valid);
+  uint32_t key[kPer];
+  bool valid[kPer];
+  load_emit(a, k, k.p0 + 64 * kPer * wave, key, valid);
   uint32_t D = 0u, Tn = 0u;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     bool def, tie;
     emit_flags(key[j], hs.kappa, def, tie);
     D += (uint32_t)__popcll(__ballot(valid[j] && def));
@@ -503,9 +532,9 @@ __device__ __forceinline__ uint32_t rank_below(unsigned long long m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// ---- ordered writes: wave w of a chunk owns its positions [1024 w, 1024 w +
-// 1024) in rows of 64; ranks come from the earlier chunks' counts, the earlier
-// waves' counts and ballots inside a row
+// ---- ordered writes: wave w of a chunk owns its positions [64 kPer w,
+// 64 kPer (w + 1)) in rows of 64; ranks come from the earlier chunks' counts,
+// the earlier waves' counts and ballots inside a row
 __global__ __launch_bounds__(kT) void lsel_emit(const float* __restrict__ z, LselArgs a, LselGeom g,
                                                 char* base, int32_t* __restrict__ idx) {
   __shared__ uint32_t rd[kT / 64], rt[kT / 64];
@@ -529,13 +558,13 @@ __global__ __launch_bounds__(kT) void lsel_emit(const float* __restrict__ z, Lse
       T0 += __shfl_xor(T0, off);
     }
   }
-  uint32_t key[16];
-  bool valid[16];
-  const int64_t base_p = k.p0 + 1024 * wave;
+  uint32_t key[kPer];
+  bool valid[kPer];
+  const int64_t base_p = k.p0 + 64 * kPer * wave;
   load_emit(a, k, base_p, key, valid);
   uint32_t D = 0u, Tn = 0u;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     bool def, tie;
     emit_flags(key[j], kap, def, tie);
     D += (uint32_t)__popcll(__ballot(valid[j] && def));
@@ -554,7 +583,7 @@ __global__ __launch_bounds__(kT) void lsel_emit(const float* __restrict__ z, Lse
   }
   int32_t* out = idx + hs.off;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     bool def, tie;
     emit_flags(key[j], kap, def, tie);
     def = def && valid[j];
