@@ -61,6 +61,8 @@ def lib():
                                  _i32p]
         L.orc_select_layer.argtypes = [_f32p, C.c_int, _i64p, C.c_int, C.c_int, _i64p, C.c_int,
                                        C.c_int, C.c_int, _i32p, _i32p]
+        L.orc_nestedkv.argtypes = [_f32p, C.c_int, _i64p, C.c_int, C.c_int, C.c_int, C.c_int,
+                                   C.c_int, C.c_void_p, C.c_double, _f32p, C.c_void_p, C.c_void_p]
         L.orc_compact_layer.argtypes = [C.c_void_p, C.c_void_p, _i32p, _i32p, C.c_int, C.c_int,
                                         _i64p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.orc_compact.argtypes = [C.c_void_p, C.c_void_p, _i32p, C.c_int, C.c_int, _i64p, _i64p,
@@ -142,6 +144,24 @@ def select(z, seqlens, kept, n_sink, n_recent):
     idx = np.zeros((L, Hkv, int(kp.sum())), np.int32)
     _check(lib().orc_select(z, sl.size, sl, L, Hkv, kp, int(n_sink), int(n_recent), idx))
     return idx
+
+
+def nestedkv(k, seqlens, nblocks=32, window=64, log_prior=(0.0, 0.0, 0.0), theta=0.1,
+             want_parts=False):
+    """NestedKV key-only score: k float32 [L][Hkv][T][d] -> s [L][Hkv][T]; with
+    want_parts also the anomalies [L][Hkv][T][3] (stable, episodic, current)
+    and the blend weights [L][B][Hkv][3]."""
+    k = _c(k, np.float32)
+    L, Hkv, T, d = k.shape
+    sl = _c(seqlens, np.int64)
+    s = np.zeros((L, Hkv, T), np.float32)
+    lp = np.ascontiguousarray(log_prior, np.float64)
+    an = np.zeros((L, Hkv, T, 3), np.float32) if want_parts else None
+    wt = np.zeros((L, sl.size, Hkv, 3), np.float32) if want_parts else None
+    _check(lib().orc_nestedkv(k, sl.size, sl, L, Hkv, d, int(nblocks), int(window), lp.ctypes.data,
+                              float(theta), s, an.ctypes.data if an is not None else None,
+                              wt.ctypes.data if wt is not None else None))
+    return (s, an, wt) if want_parts else s
 
 
 def select_layer(z, seqlens, layer_kept, n_sink, n_recent, floor_min):

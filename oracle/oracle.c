@@ -41,6 +41,12 @@
  *       the sink and recent windows is evicted, ties to the oldest position;
  *   R11 the H2O step's attention output uses those same probabilities on the
  *       values of the same tokens (before the new token is inserted);
+ *   R13 NestedKV score: keys are normalised to unit length; the stable
+ *       memory is their sequence mean, the episodic memory the mean of
+ *       ceil(N / nblocks)-position blocks, the current memory the mean of the
+ *       trailing `window` keys (the token itself included); a scale's
+ *       discriminative power is the max minus the min of its anomaly over the
+ *       head; log_prior and the surprise threshold theta are arguments;
  *   R12 layer-wide budget: the caller gives the kept total of a (layer,
  *       sequence) over all its KV heads; each head first keeps its protected
  *       positions and a floor of its own best candidates, and the rest of
@@ -338,6 +344,123 @@ int orc_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv, co
       if (keep[i]) out[o++] = (int32_t)i;
     free(keep);
     free(cand);
+  }
+  return ORC_OK;
+}
+
+/* --------------------------------------------------------------------------
+ * NestedKV key-only score (NestedKV summary page: the continuum memory state
+ * of three key means, the outer teacher's head-adaptive blending and its
+ * surprise-gated routing).  Reading R13.  Per (layer l, KV head g, sequence
+ * b), with k^_i = k_i / |k_i| (0 for a zero key):
+ *   mu_s     the mean of k^ over the sequence;
+ *   mu_e(i)  the mean of k^ over i's block, blocks of ceil(N / nblocks)
+ *            positions from the start;
+ *   mu_c(i)  the mean of k^ over the trailing window [i - window + 1, i];
+ *   a_x(i) = -cos(k^_i, mu_x) (0 when either vector is zero);
+ *   D_x = max_i a_x - min_i a_x, w = softmax(D + log_prior);
+ *   sigma(i) = population standard deviation of (a_s, a_e, a_c);
+ *   s_i = max(a_s, a_e, a_c) when sigma(i) > theta, else sum_x w_x a_x.
+ * k [L][Hkv][T][d]; s [L][Hkv][T]; anomalies (nullable) [L][Hkv][T][3];
+ * weights (nullable) [L][B][Hkv][3].
+ * ------------------------------------------------------------------------ */
+static double cos_d(const double* x, const double* y, int d) {
+  double xy = 0.0, xx = 0.0, yy = 0.0;
+  for (int e = 0; e < d; ++e) {
+    xy += x[e] * y[e];
+    xx += x[e] * x[e];
+    yy += y[e] * y[e];
+  }
+  if (xx == 0.0 || yy == 0.0) return 0.0;
+  return xy / (sqrt(xx) * sqrt(yy));
+}
+
+int orc_nestedkv(const float* k, int B, const int64_t* seqlens, int L, int Hkv, int d, int nblocks,
+                 int window, const double* log_prior, double theta, float* s, float* anomalies,
+                 float* weights) {
+  if (nblocks < 1 || window < 1 || d < 1) return ORC_EINVAL;
+  const int64_t T = total_len(B, seqlens);
+  const int units = L * Hkv * B;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int u = 0; u < units; ++u) {
+    const int l = u / (Hkv * B), g = (u / B) % Hkv, b = u % B;
+    const int64_t N = seqlens[b];
+    const int64_t row0 = (int64_t)(l * Hkv + g) * T + seq_start(b, seqlens);
+    const float* kb = k + row0 * d;
+    double* kh = (double*)malloc((size_t)(N * d) * sizeof(double));
+    double* a = (double*)malloc((size_t)(N * 3) * sizeof(double));
+    double* mu = (double*)calloc((size_t)d, sizeof(double));
+    double* me = (double*)malloc((size_t)d * sizeof(double));
+    double* mc = (double*)malloc((size_t)d * sizeof(double));
+    for (int64_t i = 0; i < N; ++i) {
+      double nn = 0.0;
+      for (int e = 0; e < d; ++e) nn += (double)kb[i * d + e] * (double)kb[i * d + e];
+      const double inv = nn > 0.0 ? 1.0 / sqrt(nn) : 0.0;
+      for (int e = 0; e < d; ++e) kh[i * d + e] = (double)kb[i * d + e] * inv;
+    }
+    /* stable memory */
+    for (int64_t i = 0; i < N; ++i)
+      for (int e = 0; e < d; ++e) mu[e] += kh[i * d + e];
+    for (int e = 0; e < d; ++e) mu[e] /= (double)N;
+    const int64_t bs = (N + nblocks - 1) / nblocks;
+    for (int64_t i = 0; i < N; ++i) {
+      const double* x = kh + i * d;
+      /* episodic memory: i's block */
+      const int64_t m0 = (i / bs) * bs, m1 = m0 + bs < N ? m0 + bs : N;
+      for (int e = 0; e < d; ++e) me[e] = 0.0;
+      for (int64_t j = m0; j < m1; ++j)
+        for (int e = 0; e < d; ++e) me[e] += kh[j * d + e];
+      for (int e = 0; e < d; ++e) me[e] /= (double)(m1 - m0);
+      /* current memory: the trailing window */
+      const int64_t c0 = i - window + 1 > 0 ? i - window + 1 : 0;
+      for (int e = 0; e < d; ++e) mc[e] = 0.0;
+      for (int64_t j = c0; j <= i; ++j)
+        for (int e = 0; e < d; ++e) mc[e] += kh[j * d + e];
+      for (int e = 0; e < d; ++e) mc[e] /= (double)(i - c0 + 1);
+      a[i * 3 + 0] = -cos_d(x, mu, d);
+      a[i * 3 + 1] = -cos_d(x, me, d);
+      a[i * 3 + 2] = -cos_d(x, mc, d);
+    }
+    /* head-adaptive blend */
+    double w[3], D[3];
+    for (int x = 0; x < 3; ++x) {
+      double lo = a[x], hi = a[x];
+      for (int64_t i = 1; i < N; ++i) {
+        if (a[i * 3 + x] < lo) lo = a[i * 3 + x];
+        if (a[i * 3 + x] > hi) hi = a[i * 3 + x];
+      }
+      D[x] = hi - lo + (log_prior ? log_prior[x] : 0.0);
+    }
+    const double dm = D[0] > D[1] ? (D[0] > D[2] ? D[0] : D[2]) : (D[1] > D[2] ? D[1] : D[2]);
+    double den = 0.0;
+    for (int x = 0; x < 3; ++x) den += exp(D[x] - dm);
+    for (int x = 0; x < 3; ++x) w[x] = exp(D[x] - dm) / den;
+    if (weights)
+      for (int x = 0; x < 3; ++x) weights[(((int64_t)l * B + b) * Hkv + g) * 3 + x] = (float)w[x];
+    /* surprise-gated routing */
+    for (int64_t i = 0; i < N; ++i) {
+      const double* ai = a + i * 3;
+      const double mean = (ai[0] + ai[1] + ai[2]) / 3.0;
+      const double var = ((ai[0] - mean) * (ai[0] - mean) + (ai[1] - mean) * (ai[1] - mean) +
+                          (ai[2] - mean) * (ai[2] - mean)) / 3.0;
+      const double sg = sqrt(var);
+      double v;
+      if (sg > theta) {
+        v = ai[0];
+        if (ai[1] > v) v = ai[1];
+        if (ai[2] > v) v = ai[2];
+      } else {
+        v = w[0] * ai[0] + w[1] * ai[1] + w[2] * ai[2];
+      }
+      s[row0 + i] = (float)v;
+      if (anomalies)
+        for (int x = 0; x < 3; ++x) anomalies[(row0 + i) * 3 + x] = (float)ai[x];
+    }
+    free(kh);
+    free(a);
+    free(mu);
+    free(me);
+    free(mc);
   }
   return ORC_OK;
 }

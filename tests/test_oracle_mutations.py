@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = ["tests/test_oracle_score.py", "tests/test_oracle_refine.py",
         "tests/test_oracle_select.py", "tests/test_oracle_h2o.py",
-        "tests/test_oracle_select_layer.py"]
+        "tests/test_oracle_select_layer.py", "tests/test_oracle_nestedkv.py"]
 
 MUTANTS = {
     "causal-off-by-one": ("const int64_t nvis = causal ? p + 1 : N;",
@@ -62,6 +62,15 @@ MUTANTS = {
     "layer-no-floor": ("kg[cand[j].pos] = 1; /* the head's floor */", "(void)0;"),
     "layer-compact-wrong-head": ("const int64_t src = (int64_t)(l * Hkv + g) * T + cu + idx[o];",
                                  "const int64_t src = (int64_t)(l * Hkv + (g + 1) % Hkv) * T + cu + idx[o];"),
+    "nkv-window-off-by-one": ("const int64_t c0 = i - window + 1 > 0 ? i - window + 1 : 0;",
+                              "const int64_t c0 = i - window > 0 ? i - window : 0;"),
+    "nkv-block-floor": ("const int64_t bs = (N + nblocks - 1) / nblocks;",
+                        "const int64_t bs = N / nblocks > 0 ? N / nblocks : 1;"),
+    "nkv-anomaly-sign": ("a[i * 3 + 0] = -cos_d(x, mu, d);", "a[i * 3 + 0] = cos_d(x, mu, d);"),
+    "nkv-sample-std": ("(ai[2] - mean) * (ai[2] - mean)) / 3.0;", "(ai[2] - mean) * (ai[2] - mean)) / 2.0;"),
+    "nkv-routing-inverted": ("if (sg > theta) {", "if (sg < theta) {"),
+    "nkv-power-max-only": ("D[x] = hi - lo + (log_prior ? log_prior[x] : 0.0);",
+                           "D[x] = hi + (log_prior ? log_prior[x] : 0.0);"),
     "h2o-no-acc-update": ("if (P[j] >= 0) A[j] = (float)((double)A[j] + add[j]);",
                           "if (P[j] >= 0) A[j] = A[j];"),
 }
