@@ -9,6 +9,7 @@
  *   hubkv_compact  gather of the kept K/V rows into a packed cache
  *   hubkv_select_layer / hubkv_compact_layer
  *                  a layer's budget shared by its KV heads (per-head floors)
+ *   hubkv_nestedkv a second base score from the keys alone (NestedKV)
  *   h2o_step       one streaming (decode) step of H2O greedy eviction
  *
  * Conventions shared by every call
@@ -199,6 +200,35 @@ int hubkv_compact_layer(const void* k_in, const void* v_in, int dtype, const int
                         const int32_t* head_kept, int B, const int64_t* seqlens /* host */, int L,
                         int Hkv, const int64_t* layer_kept /* host [L][B] */, int d, void* k_out,
                         void* v_out, void* stream);
+
+/*
+ * hubkv_nestedkv -- key-only base score (NestedKV summary page: continuum
+ * memory state, adaptive blending and surprise-gated routing).  Per (layer l,
+ * KV head g, sequence b), with k^_i = k_i / |k_i| (0 for a zero key):
+ *   mu_s = mean of k^ over the sequence (stable memory);
+ *   mu_e(i) = mean of k^ over i's block, blocks of ceil(N_b / nblocks) keys
+ *             from the start (episodic memory);
+ *   mu_c(i) = mean of k^ over the `window` keys ending at i (current memory);
+ *   a_x(i) = -cos(k^_i, mu_x), 0 when either vector is zero;
+ *   w = softmax over x of (max_i a_x - min_i a_x + log_prior[x]);
+ *   s_i = max(a_s, a_e, a_c) when the population standard deviation of the
+ *         three exceeds theta, else sum_x w_x a_x.
+ * The pages give neither the prior nor the threshold: both are arguments
+ * (log_prior host [3], nullable = zeros).  k [L][Hkv][T][d] (dtype); s fp32
+ * [L][Hkv][T]; anomalies (nullable) fp32 [L][Hkv][T][3] (a_s, a_e, a_c);
+ * weights (nullable) fp32 [L][B][Hkv][3].  window must be 64; 1 <= nblocks
+ * <= 4096.  The scores can go to hubkv_select / hubkv_select_layer as they
+ * are (any real values order); hubkv_refine expects non-negative scores.
+ * workspace >= hubkv_nestedkv_workspace(), 256-B aligned.  Deterministic.
+ */
+size_t hubkv_nestedkv_workspace(int B, const int64_t* seqlens /* host */, int L, int Hkv, int d,
+                                int nblocks);
+
+int hubkv_nestedkv(const void* k, int dtype, int B, const int64_t* seqlens /* host */, int L,
+                   int Hkv, int d, int nblocks, int window,
+                   const float* log_prior /* host [3], nullable */, float theta, float* s,
+                   float* anomalies /* nullable */, float* weights /* nullable */,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * h2o_step -- one decode step of H2O greedy eviction on a fixed-slot cache.

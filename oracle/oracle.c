@@ -405,12 +405,14 @@ int orc_nestedkv(const float* k, int B, const int64_t* seqlens, int L, int Hkv, 
     const int64_t bs = (N + nblocks - 1) / nblocks;
     for (int64_t i = 0; i < N; ++i) {
       const double* x = kh + i * d;
-      /* episodic memory: i's block */
+      /* episodic memory: i's block (its mean is formed once per block) */
       const int64_t m0 = (i / bs) * bs, m1 = m0 + bs < N ? m0 + bs : N;
-      for (int e = 0; e < d; ++e) me[e] = 0.0;
-      for (int64_t j = m0; j < m1; ++j)
-        for (int e = 0; e < d; ++e) me[e] += kh[j * d + e];
-      for (int e = 0; e < d; ++e) me[e] /= (double)(m1 - m0);
+      if (i == m0) {
+        for (int e = 0; e < d; ++e) me[e] = 0.0;
+        for (int64_t j = m0; j < m1; ++j)
+          for (int e = 0; e < d; ++e) me[e] += kh[j * d + e];
+        for (int e = 0; e < d; ++e) me[e] /= (double)(m1 - m0);
+      }
       /* current memory: the trailing window */
       const int64_t c0 = i - window + 1 > 0 ? i - window + 1 : 0;
       for (int e = 0; e < d; ++e) mc[e] = 0.0;

@@ -11,6 +11,7 @@ Functions (names follow the C ABI):
     hubkv_refine(s, seqlens, ...)                      -> (z, beta)
     hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
     hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
+    hubkv_nestedkv(k, seqlens, ...)                    -> (s, anomalies, weights)
     hubkv_select_layer(z, seqlens, layer_kept, ...)    -> (idx, head_kept)
     hubkv_compact_layer(k, v, idx, head_kept, seqlens, layer_kept) -> (k_out, v_out)
     h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, ...) -> evicted
@@ -58,6 +59,9 @@ _SIGS = {
                                 _vp]),
     "hubkv_compact_layer": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i64p, _i, _i, _i64p, _i, _vp, _vp,
                                  _vp]),
+    "hubkv_nestedkv_workspace": (_sz, [_i, _i64p, _i, _i, _i, _i]),
+    "hubkv_nestedkv": (_i, [_vp, _i, _i, _i64p, _i, _i, _i, _i, _i, _vp, _f, _vp, _vp, _vp, _vp,
+                            _sz, _vp]),
     "h2o_step": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, _i, _f,
                       _i, _vp, _vp, _vp, _vp]),
     "hubkv_protected_count": (_i64, [_i64, _i, _i]),
@@ -219,6 +223,32 @@ def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], 
                                                 _arr64(kept), L, Hkv, d, _ptr(k_out), _ptr(v_out),
                                                 _stream(stream)))
     return k_out, v_out
+
+
+def hubkv_nestedkv(k, seqlens: Sequence[int], nblocks: int = 32, window: int = 64,
+                   log_prior=(0.0, 0.0, 0.0), theta: float = 0.1, s=None, anomalies=None,
+                   weights=None, want_parts: bool = False, workspace=None, stream=None):
+    """k [L][Hkv][T][d] -> s fp32 [L][Hkv][T] (and, with want_parts, the
+    anomalies [L][Hkv][T][3] and blend weights [L][B][Hkv][3])."""
+    torch = _torch()
+    L, Hkv, T, d = k.shape
+    B = len(seqlens)
+    sl = _arr64(seqlens)
+    if s is None:
+        s = torch.empty((L, Hkv, T), dtype=torch.float32, device=k.device)
+    if want_parts and anomalies is None:
+        anomalies = torch.empty((L, Hkv, T, 3), dtype=torch.float32, device=k.device)
+    if want_parts and weights is None:
+        weights = torch.empty((L, B, Hkv, 3), dtype=torch.float32, device=k.device)
+    nb = lib().hubkv_nestedkv_workspace(B, sl, L, Hkv, d, int(nblocks))
+    if workspace is None:
+        workspace = _workspace(nb, k.device)
+    lp = (C.c_float * 3)(*[float(x) for x in log_prior])
+    _check("hubkv_nestedkv", lib().hubkv_nestedkv(
+        _ptr(k), _dtype_code(k), B, sl, L, Hkv, d, int(nblocks), int(window),
+        C.cast(lp, C.c_void_p), float(theta), _ptr(s), _ptr(anomalies), _ptr(weights),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (s, anomalies, weights) if want_parts else s
 
 
 def hubkv_select_layer(z, seqlens: Sequence[int], layer_kept, n_sink: int, n_recent: int,

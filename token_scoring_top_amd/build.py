@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libhubkv.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["abi.cpp", "score.hip", "refine_select.hip", "compact.hip", "h2o_step.hip",
-           "select_layer.hip"]
+           "select_layer.hip", "nestedkv.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

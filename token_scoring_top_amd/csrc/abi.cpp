@@ -120,6 +120,43 @@ int make_lsel(LselArgs& a, int B, const int64_t* seqlens, int L, int Hkv, const 
   return HUBKV_OK;
 }
 
+// Fill the NestedKV table: blocks of ceil(N / nblocks) keys, tiles of at most
+// kNkvTile keys inside each block.
+int make_nkv(NkvArgs& a, int B, const int64_t* seqlens, int L, int Hkv, int d, int nblocks) {
+  if (B < 1 || B > kMaxSeqs || !seqlens || L < 1 || Hkv < 1) return HUBKV_EINVAL;
+  if ((int64_t)L * Hkv > kMaxGridY || nblocks < 1 || nblocks > 4096) return HUBKV_EINVAL;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.L = L;
+  a.Hkv = Hkv;
+  a.d = d;
+  int64_t cu = 0, tiles = 0, blks = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = seqlens[b];
+    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    const int64_t bs = (n + nblocks - 1) / nblocks;
+    const int64_t nb = (n + bs - 1) / bs;
+    const int64_t tpb = (bs + kNkvTile - 1) / kNkvTile;
+    a.N[b] = (int32_t)n;
+    a.cu[b] = cu;
+    a.bs[b] = (int32_t)bs;
+    a.nblk[b] = (int32_t)nb;
+    a.tpb[b] = (int32_t)tpb;
+    a.tile_off[b] = (int32_t)tiles;
+    a.blk_off[b] = (int32_t)blks;
+    cu += n;
+    tiles += nb * tpb;
+    blks += nb;
+  }
+  if (cu >= ((int64_t)1 << 40) || tiles > 65535 || blks > 65535) return HUBKV_EINVAL;
+  a.tile_off[B] = (int32_t)tiles;
+  a.blk_off[B] = (int32_t)blks;
+  a.ntile = (int)tiles;
+  a.nblk_total = (int)blks;
+  a.T = cu;
+  return HUBKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,6 +337,37 @@ int hubkv_compact_layer(const void* k_in, const void* v_in, int dtype, const int
     return HUBKV_EALIGN;
   return hip_status(launch_compact_layer(k_in, v_in, dtype == HUBKV_BF16 ? 2 : 4, idx, head_kept,
                                          a, d, k_out, v_out, (hipStream_t)stream));
+}
+
+size_t hubkv_nestedkv_workspace(int B, const int64_t* seqlens, int L, int Hkv, int d, int nblocks) {
+  if (d != 64 && d != 128) return 0;
+  NkvArgs a;
+  if (make_nkv(a, B, seqlens, L, Hkv, d, nblocks) != HUBKV_OK) return 0;
+  return nkv_geometry(a).bytes;
+}
+
+int hubkv_nestedkv(const void* k, int dtype, int B, const int64_t* seqlens, int L, int Hkv, int d,
+                   int nblocks, int window, const float* log_prior, float theta, float* s,
+                   float* anomalies, float* weights, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  NkvArgs a;
+  if ((rc = make_nkv(a, B, seqlens, L, Hkv, d, nblocks))) return rc;
+  if (window != 64 || !isfinite(theta)) return HUBKV_EINVAL;
+  for (int x = 0; x < 3; ++x) {
+    a.prior[x] = log_prior ? log_prior[x] : 0.f;
+    if (!isfinite(a.prior[x])) return HUBKV_EINVAL;
+  }
+  a.theta = theta;
+  if (!k || !s || !workspace) return HUBKV_EALIGN;
+  if (!aligned(k, 16) || !aligned(s, 4) || !aligned(workspace, 256) ||
+      (anomalies && !aligned(anomalies, 4)) || (weights && !aligned(weights, 4)))
+    return HUBKV_EALIGN;
+  const NkvGeom g = nkv_geometry(a);
+  if (workspace_bytes < g.bytes) return HUBKV_EWORKSPACE;
+  return hip_status(launch_nestedkv(k, dtype, a, g, (char*)workspace, anomalies, s, weights,
+                                    (hipStream_t)stream));
 }
 
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,

@@ -113,6 +113,34 @@ hipError_t launch_compact_layer(const void* k_in, const void* v_in, int elem_byt
                                 const int32_t* idx, const int32_t* head_kept, const LselArgs& a,
                                 int d, void* k_out, void* v_out, hipStream_t stream);
 
+// ---- NestedKV key-only score ----------------------------------------------------------
+constexpr int kNkvTile = 1024;  // keys per work-group tile (tiles never straddle a block)
+
+struct NkvArgs {
+  int B, L, Hkv, d;
+  int ntile;       // tiles of one (layer, head) over all sequences
+  int nblk_total;  // blocks of one (layer, head) over all sequences
+  int64_t T;
+  float theta;
+  float prior[3];
+  int32_t N[kMaxSeqs];
+  int64_t cu[kMaxSeqs];
+  int32_t bs[kMaxSeqs];    // block length of each sequence
+  int32_t nblk[kMaxSeqs];  // blocks of each sequence
+  int32_t tpb[kMaxSeqs];   // tiles per block
+  int32_t tile_off[kMaxSeqs + 1];
+  int32_t blk_off[kMaxSeqs + 1];
+};
+
+struct NkvGeom {
+  size_t off_part, off_bsum, off_bnorm, off_mm, off_an, bytes;
+};
+
+NkvGeom nkv_geometry(const NkvArgs& a);
+
+hipError_t launch_nestedkv(const void* k, int dtype, const NkvArgs& a, const NkvGeom& g, char* ws,
+                           float* anomalies, float* s, float* weights, hipStream_t stream);
+
 // ---- compaction ------------------------------------------------------------------
 hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, const int32_t* idx,
                           const SeqTable& st, int L, int Hkv, int d, void* k_out, void* v_out,
