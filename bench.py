@@ -295,6 +295,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--layer-budget", action="store_true",
                     help="prefill: one budget per layer shared by its KV heads (hubkv_select_layer)")
+    ap.add_argument("--nestedkv", action="store_true",
+                    help="prefill with the NestedKV key-only score and the layer-wide budget")
     ap.add_argument("--coverage", action="store_true",
                     help="planted-burst coverage diagnostic instead of the benchmark")
     ap.add_argument("--attn-out", action="store_true",
@@ -367,6 +369,11 @@ def main(argv=None):
     # even share
     lk = [[w.Hkv * int(kb) for kb in kept] for _ in range(L)]
     floor = int(min(kept)) // 4
+    if args.nestedkv:
+        args.layer_budget = True  # the NestedKV path allocates the layer's budget across heads
+        ws_n = torch.empty(hk.lib().hubkv_nestedkv_workspace(w.B, hk._arr64(w.seqlens), L, Hkv,
+                                                             w.d, 32),
+                           dtype=torch.uint8, device="cuda")
     if args.layer_budget:
         idx_l = torch.empty(L * Hkv * Ksum, dtype=torch.int32, device="cuda")
         hkept = torch.empty((L, w.B, Hkv), dtype=torch.int32, device="cuda")
@@ -384,13 +391,20 @@ def main(argv=None):
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal, s=s, head_stats=st,
-                       workspace=ws_s, stream=stream)
-        if ev: ev[1].record(stream)
-        hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
-                        beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
-                        workspace=ws_r, stream=stream)
-        if ev: ev[2].record(stream)
+        if args.nestedkv:
+            # key-only score: no queries, no refinement (the scores are not
+            # attention mass); they go straight to the layer-wide selection
+            hk.hubkv_nestedkv(Kd, w.seqlens, s=z, workspace=ws_n, stream=stream)
+            if ev: ev[1].record(stream)
+            if ev: ev[2].record(stream)
+        else:
+            hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal, s=s, head_stats=st,
+                           workspace=ws_s, stream=stream)
+            if ev: ev[1].record(stream)
+            hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                            beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
+                            workspace=ws_r, stream=stream)
+            if ev: ev[2].record(stream)
         if args.layer_budget:
             hk.hubkv_select_layer(z, w.seqlens, lk, w.n_sink, w.n_recent, floor, idx=idx_l,
                                   head_kept=hkept, workspace=ws_l, stream=stream)
@@ -428,6 +442,8 @@ def main(argv=None):
     value = tokens / (ms_step / 1e3)
 
     nb = op_bytes(w, Ksum, elem)
+    if args.nestedkv:
+        nb["score"] = w.L * w.Hkv * w.T * (w.d * elem + 4)  # K read once, s written
     dom = max(op_ms, key=op_ms.get)
     traffic = None
     if (dom == "score" and SCORE_TRAFFIC is not None and SCORE_TRAFFIC["workload"] == w.wid
@@ -443,6 +459,8 @@ def main(argv=None):
                "select": ("lsel_init + lsel_floor_level<0..2> + lsel_pool_level<0..2> + lsel_count"
                           " + lsel_emit_count + lsel_emit") if args.layer_budget else "select_kernel",
                "compact": "compact_layer_kernel" if args.layer_budget else "compact_kernel"}
+    if args.nestedkv:
+        kernels["score"] = "nkv_tile_sum + nkv_block_sum + nkv_anomaly + nkv_route"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -462,7 +480,13 @@ def main(argv=None):
         q0, k0, v0 = q0[None], k0[None], v0[None]
         reps, tc0 = 0, time.perf_counter()
         while True:
-            if args.layer_budget:
+            if args.nestedkv:
+                z0 = oracle.nestedkv(k0, ws.seqlens)
+                kb0 = ws.kept()
+                i0, h0 = oracle.select_layer(z0, ws.seqlens, [[ws.Hkv * int(x) for x in kb0]],
+                                             ws.n_sink, ws.n_recent, int(min(kb0)) // 4)
+                oracle.compact_layer(k0, v0, i0, h0, ws.seqlens)
+            elif args.layer_budget:
                 s0, st0 = oracle.score(q0, k0, ws.seqlens, ws.W, ws.scale, ws.causal)
                 z0 = oracle.refine(s0, ws.seqlens, oracle.beta(st0, ws.seqlens, ws.beta_lo,
                                                               ws.beta_hi), ws.pool, ws.gamma, ws.r)
@@ -498,6 +522,7 @@ def main(argv=None):
                    "Hkv": w.Hkv, "d": w.d, "window": w.W, "budget": w.budget, "r": w.r,
                    "n_sink": w.n_sink, "n_recent": w.n_recent, "kept_per_head": int(Ksum),
                    "budget_scope": "layer" if args.layer_budget else "head",
+                   "scorer": "nestedkv" if args.nestedkv else "attention-mass",
                    "head_floor": floor if args.layer_budget else None,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -507,8 +532,9 @@ def main(argv=None):
         "refine_select_compact": {"ms": rsc_ms, "bytes": rsc_bytes,
                                   "GBs": rsc_bytes / (rsc_ms / 1e3) / 1e9,
                                   "frac_hbm": rsc_bytes / (rsc_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
-        "score_mfma": {"flops_one_sweep": score_flops(w), "util": mfma_util,
-                       "peak_tflops": BF16_PEAK_TFLOPS},
+        "score_mfma": None if args.nestedkv else {"flops_one_sweep": score_flops(w),
+                                                  "util": mfma_util,
+                                                  "peak_tflops": BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

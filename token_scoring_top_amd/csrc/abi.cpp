@@ -130,10 +130,12 @@ int make_nkv(NkvArgs& a, int B, const int64_t* seqlens, int L, int Hkv, int d, i
   a.L = L;
   a.Hkv = Hkv;
   a.d = d;
-  int64_t cu = 0, tiles = 0, blks = 0;
+  int64_t cu = 0, tiles = 0, blks = 0, ats = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t n = seqlens[b];
     if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    a.at_off[b] = (int32_t)ats;
+    ats += (n + kNkvAnTile - 1) / kNkvAnTile;
     const int64_t bs = (n + nblocks - 1) / nblocks;
     const int64_t nb = (n + bs - 1) / bs;
     const int64_t tpb = (bs + kNkvTile - 1) / kNkvTile;
@@ -148,7 +150,9 @@ int make_nkv(NkvArgs& a, int B, const int64_t* seqlens, int L, int Hkv, int d, i
     tiles += nb * tpb;
     blks += nb;
   }
-  if (cu >= ((int64_t)1 << 40) || tiles > 65535 || blks > 65535) return HUBKV_EINVAL;
+  if (cu >= ((int64_t)1 << 40) || tiles > 65535 || blks > 65535 || ats > 65535) return HUBKV_EINVAL;
+  a.at_off[B] = (int32_t)ats;
+  a.nat = (int)ats;
   a.tile_off[B] = (int32_t)tiles;
   a.blk_off[B] = (int32_t)blks;
   a.ntile = (int)tiles;

@@ -114,12 +114,14 @@ hipError_t launch_compact_layer(const void* k_in, const void* v_in, int elem_byt
                                 int d, void* k_out, void* v_out, hipStream_t stream);
 
 // ---- NestedKV key-only score ----------------------------------------------------------
-constexpr int kNkvTile = 1024;  // keys per work-group tile (tiles never straddle a block)
+constexpr int kNkvTile = 1024;    // keys per sum tile (sum tiles never straddle a block)
+constexpr int kNkvAnTile = 2048;  // keys per anomaly tile
 
 struct NkvArgs {
   int B, L, Hkv, d;
   int ntile;       // tiles of one (layer, head) over all sequences
   int nblk_total;  // blocks of one (layer, head) over all sequences
+  int nat;         // anomaly tiles of one (layer, head) over all sequences
   int64_t T;
   float theta;
   float prior[3];
@@ -130,6 +132,7 @@ struct NkvArgs {
   int32_t tpb[kMaxSeqs];   // tiles per block
   int32_t tile_off[kMaxSeqs + 1];
   int32_t blk_off[kMaxSeqs + 1];
+  int32_t at_off[kMaxSeqs + 1];  // first anomaly tile of each sequence
 };
 
 struct NkvGeom {
