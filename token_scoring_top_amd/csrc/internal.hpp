@@ -136,7 +136,7 @@ struct NkvArgs {
 };
 
 struct NkvGeom {
-  size_t off_part, off_bsum, off_bnorm, off_mm, off_an, bytes;
+  size_t off_part, off_bsum, off_bnorm, off_mm, off_an, off_inv, bytes;
 };
 
 NkvGeom nkv_geometry(const NkvArgs& a);

@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kT = 256;
 constexpr int kWaves = kT / 64;
-constexpr int kWin = 64;   // current-memory window
+
 
 template <typename T>
 __device__ __forceinline__ float to_f(T x);
@@ -44,6 +44,21 @@ template <>
 __device__ __forceinline__ float to_f<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f<__bf16>(__bf16 x) { return (float)x; }
+
+// Inclusive prefix sum across the 64 lanes of a wave with DPP moves (no LDS):
+// shifts by 1, 2, 4 and 8 inside each 16-lane row, then row broadcasts of lane
+// 15 into rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes whose source
+// falls outside their row add 0.
+__device__ __forceinline__ float dpp_add(float v, int y) { return v + __int_as_float(y); }
+__device__ __forceinline__ float wave_prefix(float v) {
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
 
 struct Tile {
   int lh, b, m, j;
@@ -98,12 +113,13 @@ struct Piece {
   }
 };
 
-// ---- 1: tile sums of the normalised keys.  Each wave loads RPW rows per
-// instruction, kUnroll instructions in flight; the norm of a row is folded
-// over its LPR lanes.
+// ---- 1: tile sums of the normalised keys, and every row's inverse norm.
+// Each wave loads RPW rows per instruction, kUnroll instructions in flight;
+// the norm of a row is folded over its LPR lanes.
 template <typename T, int D>
 __global__ __launch_bounds__(kT) void nkv_tile_sum(const T* __restrict__ K, NkvArgs a,
                                                    NkvGeom g, char* ws) {
+  float* invn = (float*)(ws + g.off_inv);  // every row's inverse norm, for the anomaly pass
   using PC = Piece<T, D>;
   constexpr int P = PC::P, LPR = PC::LPR, RPW = PC::RPW;
   constexpr int kUnroll = 4;
@@ -133,6 +149,7 @@ __global__ __launch_bounds__(kT) void nkv_tile_sum(const T* __restrict__ K, NkvA
       const float inv = (in[u] && nn > 0.f) ? 1.f / sqrtf(nn) : 0.f;
 #pragma unroll
       for (int i = 0; i < P; ++i) acc[i] = fmaf(x[u][i], inv, acc[i]);
+      if (in[u] && c == 0) invn[t.row_base + r0 + (int64_t)u * STEP] = inv;
     }
   }
   // rows of the wave's slots, then the waves, in a fixed order
@@ -185,20 +202,31 @@ __global__ __launch_bounds__(kT) void nkv_block_sum(NkvArgs a, NkvGeom g, char* 
   if (threadIdx.x == 0) ((float*)(ws + g.off_bnorm))[(int64_t)lh * a.nblk_total + bi] = sqrtf(n2);
 }
 
-// ---- 3: anomalies over tiles of up to kNkvAnTile rows (they may cross
-// blocks).  A walker -- the LPR lanes of one row slot of a wave -- owns a
-// contiguous run of the tile's rows and steps through it one row at a time,
-// all walkers of the work-group in lockstep, after 64 warm-up steps over the
-// rows before its run.  The window sum S is carried in the walker's lanes
-// (S += k^_new - k^_old, the row 64 back reloaded from cache); lane
-// (step mod 64) of register ring[w] keeps walker w's inverse norm of that
-// step's row, read and written with a uniform lane index.
+// ---- 3: anomalies over tiles of kNkvAnTile rows, rows on lanes.  Wave w
+// owns NSEG segments of 64 rows; in segment s lane l owns row r = 64 s + l of
+// the wave's run.  The window of the 64 rows ending at r is the segment's
+// rows up to r plus the previous segment's rows after position l, so for each
+// 16-element group of the head dimension
+//   S = (inclusive prefix of k^ across the lanes)
+//     + (exclusive suffix across the lanes of the previous segment's k^),
+// the previous segment's line reloaded from cache and renormalised with its
+// stored inverse norm (pass 1 wrote every row's); the scans are DPP moves and
+// the suffix is the previous segment's total minus its prefix.  The dot
+// products k^.S, S.S, k^.mu_s and k^.mu_e are then lane-local.  A row's
+// episodic memory is its block's; a segment's blocks are walked with uniform
+// loads (at most two when blocks hold 64 rows or more).  The wave's
+// (segment, group) items run in order with kPf items' lines in flight.
 template <typename T, int D>
 __global__ __launch_bounds__(kT) void nkv_anomaly(const T* __restrict__ K, NkvArgs a, NkvGeom g,
                                                   char* ws, float* __restrict__ an) {
-  using PC = Piece<T, D>;
-  constexpr int P = PC::P, LPR = PC::LPR, RPW = PC::RPW;
-  constexpr int NWALK = kWaves * RPW;
+  constexpr int EPW = 16 / (int)sizeof(T);     // elements per 16-byte word
+  constexpr int G = 16;                        // elements per scan group
+  constexpr int WPG = G / EPW;                 // 16-byte words per group
+  constexpr int NG = D / G;
+  constexpr int NSEG = kNkvAnTile / (kWaves * 64);
+  constexpr int kPf = 3;
+  __shared__ float mus[D];
+  __shared__ float red[kWaves];
   __shared__ float mm_s[kWaves][6];
   const int lh = blockIdx.y, x = blockIdx.x;
   int b = 0;
@@ -208,150 +236,121 @@ __global__ __launch_bounds__(kT) void nkv_anomaly(const T* __restrict__ K, NkvAr
   const int64_t t1 = t0 + kNkvAnTile < N ? t0 + kNkvAnTile : N;
   const int64_t row_base = (int64_t)lh * a.T + a.cu[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane % LPR, slot = lane / LPR;
-  const int walker = wave * RPW + slot;
   const float* bsum = (const float*)(ws + g.off_bsum) + ((int64_t)lh * a.nblk_total + a.blk_off[b]) * D;
   const float* bnrm = (const float*)(ws + g.off_bnorm) + (int64_t)lh * a.nblk_total + a.blk_off[b];
-  // the sequence sum, from the block sums in order, and its norm
-  float ms[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) ms[i] = 0.f;
-  // (unrolled so the block sums' loads are in flight together; added in order)
+  const float* invn = (const float*)(ws + g.off_inv) + row_base;
+  // the sequence sum (block sums in order) and its norm
+  {
+    const int e = threadIdx.x;
+    float v = 0.f;
+    if (e < D) {
 #pragma unroll 8
-  for (int m = 0; m < a.nblk[b]; ++m)
+      for (int m = 0; m < a.nblk[b]; ++m) v += bsum[(int64_t)m * D + e];
+      mus[e] = v;
+    }
+    float q = e < D ? v * v : 0.f;
 #pragma unroll
-    for (int i = 0; i < P; ++i) ms[i] += bsum[(int64_t)m * D + c * P + i];
+    for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off);
+    if (lane == 0) red[wave] = q;
+  }
+  __syncthreads();
   float msn = 0.f;
-#pragma unroll
-  for (int i = 0; i < P; ++i) msn = fmaf(ms[i], ms[i], msn);
-  msn = PC::row_sum(msn);
+  for (int w = 0; w < kWaves; ++w) msn += red[w];
   const float ims = msn > 0.f ? 1.f / sqrtf(msn) : 0.f;
-  // this walker's run
-  const int64_t len = t1 - t0;
-  const int64_t R = (len + NWALK - 1) / NWALK;
-  const int64_t st = t0 + R * walker < t1 ? t0 + R * walker : t1;
-  const int64_t run = st + R < t1 ? R : t1 - st;
   const int bsz = a.bs[b];
-  int cm = (int)(st / bsz);  // block of the current row, its sum and inverse norm
-  float me[P], ime;
-  auto load_block = [&](int m) {
-    const int mc = m < a.nblk[b] ? m : a.nblk[b] - 1;
-#pragma unroll
-    for (int i = 0; i < P; ++i) me[i] = bsum[(int64_t)mc * D + c * P + i];
-    const float n = bnrm[mc];
-    ime = n > 0.f ? 1.f / n : 0.f;
-  };
-  load_block(cm);
-  float S[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) S[i] = 0.f;
-  float ring[RPW];
-#pragma unroll
-  for (int w = 0; w < RPW; ++w) ring[w] = 0.f;
+  const int64_t wbase = t0 + (int64_t)wave * NSEG * 64;
   float mx[3] = {-INFINITY, -INFINITY, -INFINITY}, mn[3] = {INFINITY, INFINITY, INFINITY};
   float* anb = an + row_base * 3;
-  // Steps in groups of kPf.  The next group's rows are in flight while a
-  // group is processed in phases, so the reductions of its steps overlap:
-  // the rows' norms, the ring and the window sums (the only step-to-step
-  // dependency, a few adds), then the four dot products of every step.
-  constexpr int kPf = 4;
-  const int64_t Rmax = R;
-  u32x4 nq[kPf], oq[kPf];
-  auto issue = [&](int64_t jg) {
+  const int64_t wend = wbase + (int64_t)NSEG * 64 < t1 ? wbase + (int64_t)NSEG * 64 : t1;
+  const int nseg = wend > wbase ? (int)((wend - wbase + 63) / 64) : 0;
+  const int items = nseg * NG;
+  u32x4 buf[kPf][2 * WPG];  // the current and the previous segment's words of an item
+  auto issue = [&](int t, u32x4 (&dst)[2 * WPG]) {
+    const int s2 = t / NG, gi = t - s2 * NG;
+    const int64_t row = wbase + 64 * s2 + lane, prow = row - 64;
+    const T* cur = K + (row_base + (row < N ? row : 0)) * D + gi * G;
+    const T* prv = K + (row_base + (prow >= 0 ? prow : 0)) * D + gi * G;
 #pragma unroll
-    for (int u = 0; u < kPf; ++u) {
-      const int64_t j = jg + u, q = st + j;
-      const bool live = j < run && q >= 0;
-      const bool drop = j >= 0 && j < run && q - kWin >= 0;
-      nq[u] = PC::raw(K, row_base + (live ? q : 0), c);
-      oq[u] = PC::raw(K, row_base + (drop ? q - kWin : 0), c);
+    for (int k = 0; k < WPG; ++k) {
+      dst[k] = ((const u32x4*)cur)[k];
+      dst[WPG + k] = ((const u32x4*)prv)[k];
     }
   };
-  issue(-kWin);
-  for (int64_t jg = -kWin; jg < Rmax; jg += kPf) {
-    u32x4 cn[kPf], co[kPf];
+#pragma unroll
+  for (int u = 0; u < kPf; ++u)
+    if (u < items) issue(u, buf[u]);
+  int64_t row = 0;
+  bool inseq = false;
+  float iv = 0.f, ivp = 0.f, d_c = 0.f, s_s = 0.f, d_s = 0.f, d_e = 0.f;
+  int mfirst = 0, mlast = 0, mine = 0;
+  for (int tb = 0; tb < items; tb += kPf) {
 #pragma unroll
     for (int u = 0; u < kPf; ++u) {
-      cn[u] = nq[u];
-      co[u] = oq[u];
-    }
-    if (jg + kPf < Rmax) issue(jg + kPf);
-    // norms of the group's new rows
-    float inv[kPf];
-#pragma unroll
-    for (int u = 0; u < kPf; ++u) {
-      float xn[P];
-      PC::unpack(cn[u], xn);
-      float nn = 0.f;
-#pragma unroll
-      for (int i = 0; i < P; ++i) nn = fmaf(xn[i], xn[i], nn);
-      inv[u] = nn;
-    }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1)
-#pragma unroll
-      for (int u = 0; u < kPf; ++u) inv[u] += __shfl_xor(inv[u], off);
-    // ring, window sums and the lane partials of each step's dot products
-    // (with the inverse norm of the step's own block: a later step of the
-    // group may move to the next block)
-    float pd[kPf][4], pie[kPf];
-#pragma unroll
-    for (int u = 0; u < kPf; ++u) {
-      const int64_t j = jg + u, q = st + j;
-      const bool live = j < Rmax && j < run && q >= 0;
-      const bool drop = j >= 0 && j < run && q - kWin >= 0;
-      const float iv = (live && inv[u] > 0.f) ? 1.f / sqrtf(inv[u]) : 0.f;
-      inv[u] = iv;
-      const int L = (int)(j & (kWin - 1));
-      float iold = 0.f;
-#pragma unroll
-      for (int w = 0; w < RPW; ++w) {
-        const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ring[w]), L));
-        if (slot == w) iold = o;
-        const float nv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(iv), w * LPR));
-        if (j < Rmax) ring[w] = lane == L ? nv : ring[w];
+      const int t = tb + u;
+      if (t >= items) break;
+      const int s2 = t / NG, gi = t - s2 * NG;
+      if (gi == 0) {
+        const int64_t r0 = wbase + 64 * s2;
+        row = r0 + lane;
+        const int64_t prow = row - 64;
+        inseq = row < N;
+        iv = inseq ? invn[row] : 0.f;
+        ivp = prow >= 0 ? invn[prow] : 0.f;
+        const int64_t rl = r0 + 63 < t1 - 1 ? r0 + 63 : t1 - 1;
+        mfirst = (int)(r0 / bsz);
+        mlast = (int)(rl / bsz);
+        mine = (int)((inseq && row < t1 ? row : rl) / bsz);
+        d_c = s_s = d_s = d_e = 0.f;
       }
-      float xn[P], xo[P];
-      PC::unpack(cn[u], xn);
-      PC::unpack(co[u], xo);
-      float dc = 0.f, ss = 0.f, ds = 0.f, de = 0.f;
-      if (j >= 0 && live && q >= (int64_t)(cm + 1) * bsz) load_block(++cm);
+      float p[G], q[G], kh[G];
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const float kh = xn[i] * iv;
-        S[i] = S[i] + kh - (drop ? xo[i] * iold : 0.f);
-        dc = fmaf(kh, S[i], dc);
-        ss = fmaf(S[i], S[i], ss);
-        ds = fmaf(kh, ms[i], ds);
-        de = fmaf(kh, me[i], de);
+      for (int k = 0; k < WPG; ++k) {
+        const T* ec = (const T*)&buf[u][k];
+        const T* ep = (const T*)&buf[u][WPG + k];
+#pragma unroll
+        for (int i = 0; i < EPW; ++i) {
+          kh[k * EPW + i] = to_f<T>(ec[i]) * iv;
+          q[k * EPW + i] = to_f<T>(ep[i]) * ivp;
+        }
       }
-      pd[u][0] = dc;
-      pd[u][1] = ss;
-      pd[u][2] = ds;
-      pd[u][3] = de;
-      pie[u] = ime;
-    }
+      // the slot is free: the lines kPf items ahead go into it
+      if (t + kPf < items) issue(t + kPf, buf[u]);
 #pragma unroll
-    for (int off = 1; off < LPR; off <<= 1)
+      for (int i = 0; i < G; ++i) {
+        p[i] = wave_prefix(kh[i]);
+        const float pq = wave_prefix(q[i]);
+        q[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pq), 63)) - pq;
+      }
 #pragma unroll
-      for (int u = 0; u < kPf; ++u)
+      for (int j = 0; j < G; ++j) {
+        const float S = p[j] + q[j];
+        d_c = fmaf(kh[j], S, d_c);
+        s_s = fmaf(S, S, s_s);
+        d_s = fmaf(kh[j], mus[gi * G + j], d_s);
+      }
+      for (int m = mfirst; m <= mlast; ++m) {
+        const float* em = bsum + (int64_t)m * D + gi * G;
+        float e = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) pd[u][v] += __shfl_xor(pd[u][v], off);
-#pragma unroll
-    for (int u = 0; u < kPf; ++u) {
-      const int64_t j = jg + u, q = st + j;
-      if (j < 0 || j >= run) continue;  // warm-up steps and past the run
-      const float sn = pd[u][1] > 0.f ? sqrtf(pd[u][1]) : 0.f;
-      const float as = -(pd[u][2] * ims);
-      const float ae = -(pd[u][3] * pie[u]);
-      const float ac = sn > 0.f ? -(pd[u][0] / sn) : -0.f;
-      mx[0] = fmaxf(mx[0], as);
-      mx[1] = fmaxf(mx[1], ae);
-      mx[2] = fmaxf(mx[2], ac);
-      mn[0] = fminf(mn[0], as);
-      mn[1] = fminf(mn[1], ae);
-      mn[2] = fminf(mn[2], ac);
-      if (c < 3) anb[q * 3 + c] = c == 0 ? as : (c == 1 ? ae : ac);
+        for (int j = 0; j < G; ++j) e = fmaf(kh[j], em[j], e);
+        if (m == mine) d_e += e;
+      }
+      if (gi == NG - 1 && inseq && row < t1) {
+        const float en = bnrm[mine];
+        const float sn = s_s > 0.f ? sqrtf(s_s) : 0.f;
+        const float as = -(d_s * ims);
+        const float ae = en > 0.f ? -(d_e / en) : -0.f;
+        const float ac = sn > 0.f ? -(d_c / sn) : -0.f;
+        mx[0] = fmaxf(mx[0], as);
+        mx[1] = fmaxf(mx[1], ae);
+        mx[2] = fmaxf(mx[2], ac);
+        mn[0] = fminf(mn[0], as);
+        mn[1] = fminf(mn[1], ae);
+        mn[2] = fminf(mn[2], ac);
+        anb[row * 3 + 0] = as;
+        anb[row * 3 + 1] = ae;
+        anb[row * 3 + 2] = ac;
+      }
     }
   }
 #pragma unroll
@@ -484,6 +483,7 @@ NkvGeom nkv_geometry(const NkvArgs& a) {
   g.off_bnorm = take((size_t)LH * a.nblk_total * 4);
   g.off_mm = take((size_t)LH * a.nat * 6 * 4);
   g.off_an = take((size_t)LH * a.T * 3 * 4);
+  g.off_inv = take((size_t)LH * a.T * 4);
   g.bytes = o;
   return g;
 }
