@@ -35,9 +35,9 @@ MUTANTS = {
                               "const float qi = hub ? gamma * si : si;"),
     "gate-sign": ("const float dlt = t - si;", "const float dlt = si - t;"),
     "gate-r-not-squared": ("const float r2 = r * r;", "const float r2 = r;"),
-    "topk-ascending": ("if (x->z > y->z) return -1;", "if (x->z < y->z) return -1;"),
-    "tie-to-newest": ("return (x->pos < y->pos) ? -1 : (x->pos > y->pos ? 1 : 0);",
-                      "return (x->pos > y->pos) ? -1 : (x->pos < y->pos ? 1 : 0);"),
+    "topk-ascending": ("if (x->z > y->z) return -1; /* descending", "if (x->z < y->z) return -1; /* descending"),
+    "tie-to-newest": ("    if (x->z < y->z) return 1;\n  }\n  return (x->pos < y->pos) ? -1 : (x->pos > y->pos ? 1 : 0);",
+                      "    if (x->z < y->z) return 1;\n  }\n  return (x->pos > y->pos) ? -1 : (x->pos < y->pos ? 1 : 0);"),
     "recent-window-short": ("const int prot = (i < n_sink) || (i >= N - n_recent);",
                             "const int prot = (i < n_sink) || (i > N - n_recent);"),
     "h2o-new-token-not-candidate": ("for (int j = -1; j < C; ++j) {", "for (int j = 0; j < C; ++j) {"),
@@ -76,6 +76,11 @@ MUTANTS = {
 }
 
 
+# the pin files that exercise each family of mutants (the rest run them all)
+FAMILY = {"h2o-": ["tests/test_oracle_h2o.py"], "layer-": ["tests/test_oracle_select_layer.py"],
+          "nkv-": ["tests/test_oracle_nestedkv.py"]}
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
@@ -88,5 +93,6 @@ def test_pins_catch_mutant(name, tmp_path):
                            "-shared", str(mut), "-o", str(lib), "-lm"])
     env = dict(os.environ, HUBKV_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        *PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+                        *next((v for k, v in FAMILY.items() if name.startswith(k)), PINS)],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
