@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "ec0eab8be41358fae9004b4a505bbae034b681947ff1d8b7e7a1d1812978f123", "workload": 2,
-                 "fetch_bytes": 546601384, "write_bytes": 4350819}
+SCORE_TRAFFIC = {"sha256": "1d2eca2262eea7c2f59dd08be44d38ba80803277f6c5d8e4dbe3099a26d4fc82", "workload": 2,
+                 "fetch_bytes": 546601439, "write_bytes": 4350889}
 
 
 def _score_source_sha() -> str:
