@@ -156,11 +156,24 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(
   float* zb = z + (int64_t)lh * T + st.cu[b];
   const int lb = l * st.B + b;
   const int u = lb * Hkv + g;
-  // tile[j] holds s[i0 - half + j] (0 outside the sequence, never read)
-  for (int j = threadIdx.x; j < kRefineTile + 2 * half; j += kRefineThreads) {
-    const int i = i0 - half + j;
-    tile[j] = (i >= 0 && i < N) ? sb[i] : 0.f;
+  // tile[j] holds s[i0 - half + j] (0 outside the sequence, never read);
+  // every load is issued before the first LDS store
+  constexpr int kPer = kRefineTile / kRefineThreads;
+  const int tid = threadIdx.x;
+  float v[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int i = i0 + e * kRefineThreads + tid;
+    v[e] = i < N ? sb[i] : 0.f;
   }
+  float hv = 0.f;
+  if (tid < 2 * half) {  // halo: half positions on each side of the tile
+    const int i = tid < half ? i0 - half + tid : i0 + kRefineTile - half + tid;
+    hv = (i >= 0 && i < N) ? sb[i] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) tile[half + e * kRefineThreads + tid] = v[e];
+  if (tid < 2 * half) tile[tid < half ? tid : kRefineTile + tid] = hv;
   if (threadIdx.x < 64) {
     const float bt = beta_in ? beta_in[u] : head_beta(st, lb, b, g, Hkv, stats, lo, hi);
     if (threadIdx.x == 0) {

@@ -204,6 +204,25 @@ __device__ bool find_top(const uint32_t* hist, int nb, uint32_t need, uint32_t* 
   return ok;
 }
 
+// Copies the first nb bins of a global histogram into LDS (kBins entries, the
+// rest zero) with every load in flight at once, then clears the global bins
+// for the next launch.
+__device__ __forceinline__ void take_hist(uint32_t* gh, int nb, uint32_t* hist) {
+  constexpr int E = kBins / kT;
+  uint32_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * kT + threadIdx.x;
+    v[e] = i < nb ? ld_ag(gh + i) : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = e * kT + threadIdx.x;
+    hist[i] = v[e];
+    if (v[e]) st_ag(gh + i, 0u);
+  }
+}
+
 // Adds the LDS histogram into the global one, then counts the work-group in.
 // Returns true (block-uniform) in the last work-group of `total`.
 __device__ bool push_and_arrive(const uint32_t* lh, uint32_t* gh, uint32_t* cnt, uint32_t total,
@@ -269,12 +288,12 @@ __global__ __launch_bounds__(kT) void lsel_floor_level(const float* __restrict__
   const Ws w = ws_of(base, g);
   const Chunk k = chunk_of(a, z);
   HeadState* hs = w.hs + k.u;
+  uint32_t key[kPer];
+  load_keys(a, k, key);     // in flight while the state is read
   if (!hs->search) return;  // uniform over the head's work-groups
   const uint32_t pfx = hs->pfx;
   for (int i = threadIdx.x; i < kBins; i += kT) hist[i] = 0u;
   __syncthreads();
-  uint32_t key[kPer];
-  load_keys(a, k, key);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint32_t x = key[j];
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(kT) void lsel_floor_level(const float* __restrict__
   uint32_t* gh = w.hh + (int64_t)k.u * kBins;
   if (!push_and_arrive(hist, gh, w.ch + k.u, (uint32_t)k.nch, &flag)) return;
   // last work-group of the head: resolve the level
-  for (int i = threadIdx.x; i < kBins; i += kT) hist[i] = i < NB ? ld_ag(gh + i) : 0u;
+  take_hist(gh, NB, hist);
   __syncthreads();
   uint32_t bin, above;
   const uint32_t need = hs->need;
@@ -303,7 +322,6 @@ __global__ __launch_bounds__(kT) void lsel_floor_level(const float* __restrict__
     }
     st_ag(w.ch + k.u, 0u);
   }
-  for (int i = threadIdx.x; i < kBins; i += kT) st_ag(gh + i, 0u);
 }
 
 // ---- pool levels: per (layer, sequence), over the candidates outside the floors
@@ -316,13 +334,13 @@ __global__ __launch_bounds__(kT) void lsel_pool_level(const float* __restrict__ 
   const Ws w = ws_of(base, g);
   const Chunk k = chunk_of(a, z);
   SegState* ss = w.ss + k.s;
+  uint32_t key[kPer];
+  load_keys(a, k, key);     // in flight while the state is read
   if (!ss->search) return;  // uniform over the (layer, sequence)
   const uint32_t pfx = ss->pfx;
   const uint32_t phi = w.hs[k.u].phi;
   for (int i = threadIdx.x; i < kBins; i += kT) hist[i] = 0u;
   __syncthreads();
-  uint32_t key[kPer];
-  load_keys(a, k, key);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint32_t x = key[j];
@@ -333,7 +351,7 @@ __global__ __launch_bounds__(kT) void lsel_pool_level(const float* __restrict__ 
   uint32_t* gh = w.hg + (int64_t)k.s * kBins;
   if (!push_and_arrive(hist, gh, w.cg + k.s, (uint32_t)(k.nch * a.Hkv), &flag)) return;
   // last work-group of the (layer, sequence): add the floors' left-out ties
-  for (int i = threadIdx.x; i < kBins; i += kT) hist[i] = i < NB ? ld_ag(gh + i) : 0u;
+  take_hist(gh, NB, hist);
   __syncthreads();
   for (int hh = threadIdx.x; hh < a.Hkv; hh += kT) {
     const HeadState& o = w.hs[(int64_t)k.s * a.Hkv + hh];
@@ -356,7 +374,6 @@ __global__ __launch_bounds__(kT) void lsel_pool_level(const float* __restrict__ 
     }
     st_ag(w.cg + k.s, 0u);
   }
-  for (int i = threadIdx.x; i < kBins; i += kT) st_ag(gh + i, 0u);
 }
 
 // ---- pool keys above / at tau per head; the last work-group of a (layer,
