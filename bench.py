@@ -65,6 +65,17 @@ def copy_calibration(reps: int = 5) -> int:
     return 0
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cores() -> int:
     try:
         return len(os.sched_getaffinity(0))
@@ -202,6 +213,7 @@ def bench_decode(args, w):
                 break
         tc = (time.perf_counter() - tc0) / reps
         cpu = {"value": C / tc, "unit": "retained-cache tokens/s/head", "cores": used,
+               "cpu_model": _cpu_model(),
                "kind": "oracle",
                "sample": f"{reps} decode step(s) of the full batch ({B} x {Hkv} heads x {C} "
                          f"slots) from a copy of the GPU state, {tc:.3f} s each"}
@@ -501,6 +513,7 @@ def main(argv=None):
                 break
         tc = (time.perf_counter() - tc0) / reps
         cpu = {"value": float(ws.T) / tc, "unit": "tokens/s/head", "cores": used, "kind": "oracle",
+               "cpu_model": _cpu_model(),
                "sample": f"{reps} prefill chain(s) of layer 0" +
                          (f", sequence 0 ({ws.T} tokens)" if w.B > 1 else f" ({ws.T} tokens)") +
                          f", {ws.Hkv} KV heads, {tc:.2f} s each"}
