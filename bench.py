@@ -453,6 +453,23 @@ def main(argv=None):
     tokens = float(w.T * w.L)
     value = tokens / (ms_step / 1e3)
 
+    # the Zipf workload's attention mass: slope of log(score) against log(rank)
+    # on layer 0 (ranks 16 .. N/16, every KV head), against the planted -alpha
+    zipf = None
+    if w.zipf_alpha is not None and not args.nestedkv:
+        s0 = s[0].cpu().numpy().astype(np.float64)
+        slopes = []
+        for h in range(w.Hkv):
+            for b in range(w.B):
+                c0 = int(sum(w.seqlens[:b]))
+                v = np.sort(s0[h, c0:c0 + w.seqlens[b]])[::-1]
+                rk = np.arange(1, v.size + 1)
+                sel = (rk >= 16) & (rk <= v.size // 16) & (v > 0)
+                slopes.append(float(np.polyfit(np.log(rk[sel]), np.log(v[sel]), 1)[0]))
+        zipf = {"planted_alpha": w.zipf_alpha, "fitted_slope_mean": float(np.mean(slopes)),
+                "fitted_slope_min": float(np.min(slopes)), "fitted_slope_max": float(np.max(slopes)),
+                "ranks": "16 .. N/16, layer 0, every KV head"}
+
     nb = op_bytes(w, Ksum, elem)
     if args.nestedkv:
         nb["score"] = w.L * w.Hkv * w.T * (w.d * elem + 4)  # K read once, s written
@@ -549,6 +566,7 @@ def main(argv=None):
                    "budget_scope": "layer" if args.layer_budget else "head",
                    "scorer": "nestedkv" if args.nestedkv else "attention-mass",
                    "head_floor": floor if args.layer_budget else None,
+                   "zipf_mass": zipf,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "op": dom,
