@@ -571,12 +571,14 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "op": dom,
                      "kernels": kernels[dom], "algorithmic_bytes": nb[dom]},
+        "token_heads_per_s": value * w.Hkv,  # aggregate over the KV heads
         "ops_ms": op_ms,
         "refine_select_compact": {"ms": rsc_ms, "bytes": rsc_bytes,
                                   "GBs": rsc_bytes / (rsc_ms / 1e3) / 1e9,
                                   "frac_hbm": rsc_bytes / (rsc_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "score_mfma": None if args.nestedkv else {"flops_one_sweep": score_flops(w),
                                                   "util": mfma_util,
+                                                  "util_executed": 2 * mfma_util,  # two sweeps
                                                   "peak_tflops": BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
     }
