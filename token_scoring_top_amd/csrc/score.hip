@@ -637,6 +637,8 @@ __global__ __launch_bounds__(64 * NRG, 2) void score_pass_shared(
       const int buf = si & 1;
       const int64_t s0 = key_begin + (int64_t)si * SK;
       if (si + 1 < nst) dma(s0 + SK, buf ^ 1);
+      // unrolled: each tile's LDS offset becomes an instruction immediate
+#pragma unroll
       for (int t = 0; t < NRG; ++t) {
         const int64_t key0 = s0 + 32 * t;
         if (key0 >= key_end) break;
@@ -678,6 +680,8 @@ __global__ __launch_bounds__(64 * NRG, 2) void score_pass_shared(
       const int buf = si & 1;
       const int64_t s0 = key_begin + (int64_t)si * SK;
       if (si + 1 < nst) dma(s0 + SK, buf ^ 1);
+      // unrolled: each tile's LDS offset becomes an instruction immediate
+#pragma unroll
       for (int t = 0; t < NRG; ++t) {
         const int64_t key0 = s0 + 32 * t;
         if (key0 >= key_end) break;
