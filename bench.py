@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "1d2eca2262eea7c2f59dd08be44d38ba80803277f6c5d8e4dbe3099a26d4fc82", "workload": 2,
-                 "fetch_bytes": 546601439, "write_bytes": 4350889}
+SCORE_TRAFFIC = {"sha256": "1eeaeb0410b0c04530eea87172224065d37a60aed16debe62d708a83d2a78ed3", "workload": 2,
+                 "fetch_bytes": 546600386, "write_bytes": 4350851}
 
 
 def _score_source_sha() -> str:
