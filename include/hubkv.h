@@ -7,6 +7,8 @@
  *   hubkv_refine   HubKV refinement of those scores before Top-K
  *   hubkv_select   per-head Top-K with protected sink and recent tokens
  *   hubkv_compact  gather of the kept K/V rows into a packed cache
+ *   hubkv_score_strided / hubkv_compact_strided
+ *                  the same on caller-strided views (token-major, padded)
  *   hubkv_select_layer / hubkv_compact_layer
  *                  a layer's budget shared by its KV heads (per-head floors)
  *   hubkv_nestedkv a second base score from the keys alone (NestedKV)
@@ -40,6 +42,12 @@
  *                                ascending within each sequence
  *   K_out, V_out [L][Hkv][sum_b kept_b][d]
  * Query head h belongs to KV head h / (Hq / Hkv) (contiguous groups).
+ * The *_strided calls take the Q, K and V operands as views instead: three
+ * element strides (layer, head, row) per operand, a host int64_t[3], d still
+ * contiguous.  Element (l, h, r, e) is at base + l*s[0] + h*s[1] + r*s[2] + e,
+ * with r the window row b*W + w of Q or the packed token / kept-row index of
+ * K and V.  Each stride is a non-negative multiple of 16 bytes; an output
+ * view must not map two (layer, head, row) triples onto the same bytes.
  *
  * Limits: 1 <= B <= 64; d in {64, 128}; Hq % Hkv == 0; (Hq/Hkv)*W <= 512;
  * W <= every sequence length; element type HUBKV_F32 or HUBKV_BF16; Q/K/V
@@ -97,6 +105,20 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
                 int L, int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
                 double* head_stats /* nullable */, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * hubkv_score_strided -- hubkv_score on strided Q and K views (same
+ * computation, same results bit for bit, same workspace size): a token-major
+ * cache [L][T][Hkv][d] is k_strides = {T*Hkv*d, d, Hkv*d}; a cache with
+ * room for more tokens per head has a larger head stride.  Strides are
+ * host int64_t[3] in elements; invalid strides return HUBKV_EINVAL, strides
+ * that are not 16-byte multiples HUBKV_EALIGN.  s and head_stats stay packed.
+ */
+int hubkv_score_strided(const void* q, const int64_t* q_strides /* host [3] */, const void* k,
+                        const int64_t* k_strides /* host [3] */, int dtype, int B,
+                        const int64_t* seqlens /* host */, int L, int Hq, int Hkv, int W, int d,
+                        float scale, int causal, float* s, double* head_stats /* nullable */,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes hubkv_refine needs (0 on invalid sizes). */
 size_t hubkv_refine_workspace(int B, const int64_t* seqlens /* host [B] */, int L, int Hkv);
@@ -156,6 +178,21 @@ int hubkv_select(const float* z, int B, const int64_t* seqlens /* host */, int L
 int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
                   const int64_t* seqlens /* host */, const int64_t* kept /* host [B] */, int L,
                   int Hkv, int d, void* k_out, void* v_out, void* stream);
+
+/*
+ * hubkv_compact_strided -- hubkv_compact between strided views: the inputs
+ * may be token-major or padded caches, and the outputs may be the first
+ * sum_b kept_b rows of larger per-head caches (row stride d, head stride the
+ * cache capacity times d).  Strides are host int64_t[3] (layer, head, row) in
+ * elements.  The output views must not overlap each other or the inputs;
+ * only the overlap of distinct rows within one output view is checked.
+ */
+int hubkv_compact_strided(const void* k_in, const int64_t* k_in_strides /* host [3] */,
+                          const void* v_in, const int64_t* v_in_strides /* host [3] */, int dtype,
+                          const int32_t* idx, int B, const int64_t* seqlens /* host */,
+                          const int64_t* kept /* host [B] */, int L, int Hkv, int d, void* k_out,
+                          const int64_t* k_out_strides /* host [3] */, void* v_out,
+                          const int64_t* v_out_strides /* host [3] */, void* stream);
 
 /*
  * hubkv_select_layer -- one budget per (layer, sequence), shared by its KV

@@ -198,3 +198,56 @@ def test_python_binding_raises_on_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(hk, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         hk.lib()
+
+
+def test_score_strided_validation():
+    L = hk.lib()
+    sl = a64([512])
+    d, Hq, Hkv, W = 64, 4, 2, 32
+    qs_ok = [Hq * W * d, W * d, d]
+    ks_ok = [Hkv * 512 * d, 512 * d, d]
+
+    def call(qs=qs_ok, ks=ks_ok, dt=1, ws=None):
+        q = None if qs is None else a64(qs)
+        k = None if ks is None else a64(ks)
+        return L.hubkv_score_strided(P, q, P, k, dt, 1, sl, 1, Hq, Hkv, W, d, 0.125, 1, P, P,
+                                     ws, 1 << 30, None)
+
+    # valid strides reach the workspace check (the last one before any launch)
+    assert call() == EWS
+    assert call(ks=[0, d, Hkv * d]) == EWS              # token-major K
+    assert call(qs=[0, W * d, d]) == EWS                # queries broadcast over layers
+    assert call(qs=None) == EINVAL
+    assert call(ks=[0, -d, d]) == EINVAL
+    assert call(ks=[0, 512 * d, 1 << 51]) == EINVAL     # stride out of range
+    assert call(ks=[0, 1 << 50, 1 << 50]) == EINVAL     # offsets beyond 2^60 bytes
+    assert call(ks=[0, 512 * d, d + 4]) == EALIGN       # bf16 row of 136 bytes
+    assert call(ks=[0, 512 * d, d + 8]) == EWS          # 144 bytes: a 16-byte multiple
+    assert call(dt=0, ks=[0, 512 * d, d + 2]) == EALIGN  # fp32 row of 264 bytes
+    assert call(dt=0, ks=[0, 512 * d, d + 4]) == EWS
+
+
+def test_compact_strided_validation():
+    L = hk.lib()
+    sl = a64([100])
+    d, Hkv = 128, 2
+    ins = [Hkv * 100 * d, 100 * d, d]
+    outs = [Hkv * 10 * d, 10 * d, d]
+
+    def call(ki=P, ks=ins, os_=outs, vos=outs, kept=(10,), dt=1):
+        return L.hubkv_compact_strided(ki, a64(ks), P, a64(ins), dt, P, 1, sl,
+                                       a64(list(kept)), 1, Hkv, d, P + (1 << 20), a64(os_),
+                                       P + (1 << 21), a64(vos), None)
+
+    # every stride valid: the misaligned K input is the first error left
+    assert call(ki=P + 8) == EALIGN
+    assert call(ki=P + 8, os_=[0, d, Hkv * d]) == EALIGN    # token-major output
+    assert call(ki=P + 8, os_=[0, 64 * d, d]) == EALIGN     # rows of a 64-row cache
+    assert call(os_=[0, 10 * d, d - 8]) == EINVAL            # rows overlap
+    assert call(os_=[0, 5 * d, d]) == EINVAL                 # heads overlap
+    assert call(os_=[0, 10 * d, 0]) == EINVAL                # every row on one
+    assert call(vos=[0, d, d]) == EINVAL                     # token and head strides equal
+    assert call(ks=[0, 100 * d, d + 4]) == EALIGN            # 264-byte bf16 rows
+    assert call(ki=P + 8, ks=[0, 0, d]) == EALIGN            # inputs may overlap (reads only)
+    # nothing is kept: no output row is addressed and nothing is launched
+    assert call(kept=(0,), os_=[0, 0, 0], vos=[0, 0, 0]) == 0

@@ -11,6 +11,9 @@ Functions (names follow the C ABI):
     hubkv_refine(s, seqlens, ...)                      -> (z, beta)
     hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
     hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
+    (q, k, v and the compaction outputs may be strided views whose last
+     axis is contiguous: those calls go to hubkv_score_strided and
+     hubkv_compact_strided)
     hubkv_nestedkv(k, seqlens, ...)                    -> (s, anomalies, weights)
     hubkv_select_layer(z, seqlens, layer_kept, ...)    -> (idx, head_kept)
     hubkv_compact_layer(k, v, idx, head_kept, seqlens, layer_kept) -> (k_out, v_out)
@@ -54,6 +57,10 @@ _SIGS = {
                           _vp]),
     "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp]),
     "hubkv_compact": (_i, [_vp, _vp, _i, _vp, _i, _i64p, _i64p, _i, _i, _i, _vp, _vp, _vp]),
+    "hubkv_score_strided": (_i, [_vp, _i64p, _vp, _i64p, _i, _i, _i64p, _i, _i, _i, _i, _i, _f,
+                                 _i, _vp, _vp, _vp, _sz, _vp]),
+    "hubkv_compact_strided": (_i, [_vp, _i64p, _vp, _i64p, _i, _vp, _i, _i64p, _i64p, _i, _i,
+                                   _i, _vp, _i64p, _vp, _i64p, _vp]),
     "hubkv_select_layer_workspace": (_sz, [_i, _i64p, _i, _i]),
     "hubkv_select_layer": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _i, _vp, _vp, _vp, _sz,
                                 _vp]),
@@ -121,14 +128,24 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _ptr(t) -> Optional[int]:
+def _ptr(t, view: bool = False) -> Optional[int]:
+    """Device address of `t`; with view=True any layout whose last axis is
+    contiguous is accepted (its strides go to a *_strided call)."""
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensors must live on the GPU")
-    if not t.is_contiguous():
+    if view:
+        if t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1):
+            raise ValueError("views must be 4-D with a contiguous last axis")
+    elif not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return t.data_ptr()
+
+
+def _strides3(t) -> C.Array:
+    """(layer, head, row) element strides of a 4-D view."""
+    return _arr64(t.stride()[:3])
 
 
 def _stream(stream=None) -> int:
@@ -164,10 +181,17 @@ def hubkv_score(q, k, seqlens: Sequence[int], W: int, scale: float, causal: bool
     nb = lib().hubkv_score_workspace(B, sl, L, Hq, Hkv, W, d, dt)
     if workspace is None:
         workspace = _workspace(nb, q.device)
-    _check("hubkv_score", lib().hubkv_score(_ptr(q), _ptr(k), dt, B, sl, L, Hq, Hkv, W, d,
-                                            float(scale), int(bool(causal)), _ptr(s),
-                                            _ptr(head_stats), _ptr(workspace),
-                                            workspace.numel(), _stream(stream)))
+    if q.is_contiguous() and k.is_contiguous():
+        _check("hubkv_score", lib().hubkv_score(_ptr(q), _ptr(k), dt, B, sl, L, Hq, Hkv, W, d,
+                                                float(scale), int(bool(causal)), _ptr(s),
+                                                _ptr(head_stats), _ptr(workspace),
+                                                workspace.numel(), _stream(stream)))
+    else:
+        _check("hubkv_score_strided",
+               lib().hubkv_score_strided(_ptr(q, True), _strides3(q), _ptr(k, True),
+                                         _strides3(k), dt, B, sl, L, Hq, Hkv, W, d, float(scale),
+                                         int(bool(causal)), _ptr(s), _ptr(head_stats),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
     return s, head_stats
 
 
@@ -210,7 +234,8 @@ def hubkv_select(z, seqlens: Sequence[int], kept: Sequence[int], n_sink: int, n_
 
 def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], k_out=None,
                   v_out=None, stream=None):
-    """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [L][Hkv][sum kept][d]."""
+    """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [L][Hkv][sum kept][d] (any of
+    the four may be a view with a contiguous last axis)."""
     torch = _torch()
     L, Hkv, T, d = k_in.shape
     K = int(sum(kept))
@@ -218,10 +243,22 @@ def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], 
         k_out = torch.empty((L, Hkv, K, d), dtype=k_in.dtype, device=k_in.device)
     if v_out is None:
         v_out = torch.empty((L, Hkv, K, d), dtype=v_in.dtype, device=v_in.device)
-    _check("hubkv_compact", lib().hubkv_compact(_ptr(k_in), _ptr(v_in), _dtype_code(k_in),
-                                                _ptr(idx), len(seqlens), _arr64(seqlens),
-                                                _arr64(kept), L, Hkv, d, _ptr(k_out), _ptr(v_out),
-                                                _stream(stream)))
+    for t, shape in ((v_in, (L, Hkv, T, d)), (k_out, (L, Hkv, K, d)), (v_out, (L, Hkv, K, d))):
+        if tuple(t.shape) != shape or t.dtype != k_in.dtype:
+            raise ValueError("inconsistent k/v shapes or dtypes")
+    dt = _dtype_code(k_in)
+    if all(t.is_contiguous() for t in (k_in, v_in, k_out, v_out)):
+        _check("hubkv_compact", lib().hubkv_compact(_ptr(k_in), _ptr(v_in), dt, _ptr(idx),
+                                                    len(seqlens), _arr64(seqlens), _arr64(kept),
+                                                    L, Hkv, d, _ptr(k_out), _ptr(v_out),
+                                                    _stream(stream)))
+    else:
+        _check("hubkv_compact_strided",
+               lib().hubkv_compact_strided(_ptr(k_in, True), _strides3(k_in), _ptr(v_in, True),
+                                           _strides3(v_in), dt, _ptr(idx), len(seqlens),
+                                           _arr64(seqlens), _arr64(kept), L, Hkv, d,
+                                           _ptr(k_out, True), _strides3(k_out),
+                                           _ptr(v_out, True), _strides3(v_out), _stream(stream)))
     return k_out, v_out
 
 

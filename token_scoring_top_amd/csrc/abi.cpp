@@ -77,6 +77,43 @@ int check_score_shape(int L, int Hq, int Hkv, int W, const SeqTable& st) {
   return HUBKV_OK;
 }
 
+// Validate the element strides (layer, head, row) of an operand whose rows
+// hold `row` contiguous elements of `esize` bytes, with `ext` layers, heads
+// and rows: every stride a non-negative multiple of 16 bytes, every offset
+// below 2^60 bytes and, for an output, distinct (layer, head, row) triples on
+// disjoint bytes.
+int check_strides(const int64_t* sd, const int64_t ext[3], int esize, int64_t row, bool output) {
+  if (!sd) return HUBKV_EINVAL;
+  for (int i = 0; i < 3; ++i) {
+    if (sd[i] < 0 || sd[i] > ((int64_t)1 << 50)) return HUBKV_EINVAL;
+    if ((sd[i] * esize) % 16) return HUBKV_EALIGN;
+  }
+  if (ext[0] < 1 || ext[1] < 1 || ext[2] < 1) return HUBKV_OK;  // nothing addressed
+  int64_t last = row;
+  for (int i = 0; i < 3; ++i) {
+    int64_t t;
+    if (__builtin_mul_overflow(sd[i], ext[i] - 1, &t) || __builtin_add_overflow(last, t, &last))
+      return HUBKV_EINVAL;
+  }
+  if (last > ((int64_t)1 << 60) / esize) return HUBKV_EINVAL;
+  if (!output) return HUBKV_OK;
+  int o[3] = {0, 1, 2};  // dimensions by ascending stride
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && sd[o[j]] < sd[o[j - 1]]; --j) {
+      const int x = o[j];
+      o[j] = o[j - 1];
+      o[j - 1] = x;
+    }
+  int64_t span = row;  // elements covered by the dimensions placed so far
+  for (int i = 0; i < 3; ++i) {
+    const int64_t n = ext[o[i]], st = sd[o[i]];
+    if (n <= 1) continue;
+    if (st < span) return HUBKV_EINVAL;
+    span = st * (n - 1) + span;
+  }
+  return HUBKV_OK;
+}
+
 // Fill the layer-wide selection table; validates shapes and budgets.
 int make_lsel(LselArgs& a, int B, const int64_t* seqlens, int L, int Hkv, const int64_t* layer_kept,
               int n_sink, int n_recent, int floor_min) {
@@ -201,9 +238,11 @@ size_t hubkv_score_workspace(int B, const int64_t* seqlens, int L, int Hq, int H
   return score_geometry(st, L, Hq, Hkv, W, d, dtype).bytes;
 }
 
-int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens, int L,
-                int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
-                double* head_stats, void* workspace, size_t workspace_bytes, void* stream) {
+int hubkv_score_strided(const void* q, const int64_t* q_strides, const void* k,
+                        const int64_t* k_strides, int dtype, int B, const int64_t* seqlens, int L,
+                        int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                        double* head_stats, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   int rc = check_dtype_d(dtype, d);
   if (rc) return rc;
   SeqTable st;
@@ -212,13 +251,41 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
   if ((rc = make_table(st, B, seqlens, chunk))) return rc;
   if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
   if (!isfinite(scale)) return HUBKV_EINVAL;
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) T += st.N[b];
+  const int esize = dtype == HUBKV_BF16 ? 2 : 4;
+  const int64_t qext[3] = {L, Hq, (int64_t)B * W}, kext[3] = {L, Hkv, T};
+  if ((rc = check_strides(q_strides, qext, esize, d, false))) return rc;
+  if ((rc = check_strides(k_strides, kext, esize, d, false))) return rc;
   if (!q || !k || !s || !aligned(q, 16) || !aligned(k, 16) || !aligned(s, 4)) return HUBKV_EALIGN;
   if (head_stats && !aligned(head_stats, 8)) return HUBKV_EALIGN;
   const ScoreGeom geo = score_geometry(st, L, Hq, Hkv, W, d, dtype);
   if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
   if (!aligned(workspace, 256)) return HUBKV_EALIGN;
-  return hip_status(launch_score(q, k, dtype, st, L, Hq, Hkv, W, d, scale, causal, s, head_stats,
-                                 (char*)workspace, geo, (hipStream_t)stream));
+  const ScoreStrides sd{q_strides[0], q_strides[1], q_strides[2],
+                        k_strides[0], k_strides[1], k_strides[2]};
+  return hip_status(launch_score(q, k, dtype, st, L, Hq, Hkv, W, d, sd, scale, causal, s,
+                                 head_stats, (char*)workspace, geo, (hipStream_t)stream));
+}
+
+int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens, int L,
+                int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                double* head_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens) return HUBKV_EINVAL;
+    T += seqlens[b];
+  }
+  // Bounds that check_score_shape implies, so the packed strides cannot overflow.
+  if (L < 1 || Hq < 1 || Hkv < 1 || W < 1 || W > 512 || Hkv > kMaxGridY || Hq > 512 * kMaxGridY)
+    return HUBKV_EINVAL;
+  const int64_t qs[3] = {(int64_t)Hq * B * W * d, (int64_t)B * W * d, d};
+  const int64_t ks[3] = {(int64_t)Hkv * T * d, T * d, d};
+  return hubkv_score_strided(q, qs, k, ks, dtype, B, seqlens, L, Hq, Hkv, W, d, scale, causal, s,
+                             head_stats, workspace, workspace_bytes, stream);
 }
 
 size_t hubkv_refine_workspace(int B, const int64_t* seqlens, int L, int Hkv) {
@@ -276,21 +343,57 @@ int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
   return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, (hipStream_t)stream));
 }
 
-int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
-                  const int64_t* seqlens, const int64_t* kept, int L, int Hkv, int d, void* k_out,
-                  void* v_out, void* stream) {
+int hubkv_compact_strided(const void* k_in, const int64_t* k_in_strides, const void* v_in,
+                          const int64_t* v_in_strides, int dtype, const int32_t* idx, int B,
+                          const int64_t* seqlens, const int64_t* kept, int L, int Hkv, int d,
+                          void* k_out, const int64_t* k_out_strides, void* v_out,
+                          const int64_t* v_out_strides, void* stream) {
   int rc = check_dtype_d(dtype, d);
   if (rc) return rc;
   SeqTable st;
   if ((rc = make_table(st, B, seqlens, kRefineTile))) return rc;
   if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
   if ((rc = check_kept(st, kept, 0, 0, false))) return rc;
+  int64_t T = 0, K = 0;
+  for (int b = 0; b < B; ++b) {
+    T += st.N[b];
+    K += st.kept[b];
+  }
+  const int esize = dtype == HUBKV_BF16 ? 2 : 4;
+  const int64_t in_ext[3] = {L, Hkv, T}, out_ext[3] = {L, Hkv, K};
+  if ((rc = check_strides(k_in_strides, in_ext, esize, d, false))) return rc;
+  if ((rc = check_strides(v_in_strides, in_ext, esize, d, false))) return rc;
+  if ((rc = check_strides(k_out_strides, out_ext, esize, d, true))) return rc;
+  if ((rc = check_strides(v_out_strides, out_ext, esize, d, true))) return rc;
   if (!k_in || !v_in || !k_out || !v_out || !idx) return HUBKV_EALIGN;
   if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
       !aligned(idx, 4))
     return HUBKV_EALIGN;
-  return hip_status(launch_compact(k_in, v_in, dtype == HUBKV_BF16 ? 2 : 4, idx, st, L, Hkv, d,
+  const int per = 16 / esize;  // elements per 16-byte unit
+  auto rows = [per](const int64_t* x) { return RowStrides{x[0] / per, x[1] / per, x[2] / per}; };
+  return hip_status(launch_compact(k_in, v_in, esize, idx, st, L, Hkv, d, rows(k_in_strides),
+                                   rows(v_in_strides), rows(k_out_strides), rows(v_out_strides),
                                    k_out, v_out, (hipStream_t)stream));
+}
+
+int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* idx, int B,
+                  const int64_t* seqlens, const int64_t* kept, int L, int Hkv, int d, void* k_out,
+                  void* v_out, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  if (B < 1 || B > kMaxSeqs || !seqlens || !kept) return HUBKV_EINVAL;
+  if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  int64_t T = 0, K = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens || kept[b] < 0 || kept[b] > seqlens[b])
+      return HUBKV_EINVAL;
+    T += seqlens[b];
+    K += kept[b];
+  }
+  const int64_t is[3] = {(int64_t)Hkv * T * d, T * d, d};
+  const int64_t os[3] = {(int64_t)Hkv * K * d, K * d, d};
+  return hubkv_compact_strided(k_in, is, v_in, is, dtype, idx, B, seqlens, kept, L, Hkv, d, k_out,
+                               os, v_out, os, stream);
 }
 
 size_t hubkv_select_layer_workspace(int B, const int64_t* seqlens, int L, int Hkv) {

@@ -59,9 +59,18 @@ int score_chunk(int B, const int64_t* seqlens, int64_t units, int rows, int dtyp
 
 ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int d, int dtype);
 
+// Element strides of the score operands; the d axis is always contiguous.
+// Q row (layer l, query head h, sequence b, window row w) starts at
+// l*q_l + h*q_h + (b*W + w)*q_r; key token t of (layer l, KV head g) at
+// l*k_l + g*k_h + t*k_t, t counted over the packed sequences.
+struct ScoreStrides {
+  int64_t q_l, q_h, q_r, k_l, k_h, k_t;
+};
+
 hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable& st, int L, int Hq,
-                        int Hkv, int W, int d, float scale, int causal, float* s,
-                        double* head_stats, char* ws, const ScoreGeom& geo, hipStream_t stream);
+                        int Hkv, int W, int d, const ScoreStrides& sd, float scale, int causal,
+                        float* s, double* head_stats, char* ws, const ScoreGeom& geo,
+                        hipStream_t stream);
 
 // ---- refine / select ---------------------------------------------------------
 constexpr int kRefineTile = 1024;
@@ -145,9 +154,17 @@ hipError_t launch_nestedkv(const void* k, int dtype, const NkvArgs& a, const Nkv
                            float* anomalies, float* s, float* weights, hipStream_t stream);
 
 // ---- compaction ------------------------------------------------------------------
+// Strides of a compaction in 16-byte units (the d axis contiguous): row t of
+// (layer l, KV head h) starts at l*s_l + h*s_h + t*s_t, t counted over the
+// packed sequences (the input) or the packed kept rows (the output).
+struct RowStrides {
+  int64_t s_l, s_h, s_t;
+};
+
 hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, const int32_t* idx,
-                          const SeqTable& st, int L, int Hkv, int d, void* k_out, void* v_out,
-                          hipStream_t stream);
+                          const SeqTable& st, int L, int Hkv, int d, const RowStrides& ki,
+                          const RowStrides& vi, const RowStrides& ko, const RowStrides& vo,
+                          void* k_out, void* v_out, hipStream_t stream);
 
 // ---- streaming H2O step ------------------------------------------------------------
 struct H2OArgs {

@@ -42,6 +42,8 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
 struct ScoreArgs {
   int L, Hq, Hkv, G, W, M, Mpad, chunk, nchunk, causal;
   int64_t T;
+  int64_t qsl, qsh, qsr;  // Q element strides: layer, query head, window row
+  int64_t ksl, ksh, kst;  // K element strides: layer, KV head, token
   float c2;  // scale * log2(e)
 };
 
@@ -104,12 +106,21 @@ ScoreGeom score_geometry(const SeqTable& st, int L, int Hq, int Hkv, int W, int 
 
 namespace {
 
+// Row r (head-local index h_local * W + w) of query group g, sequence b.
 __device__ __forceinline__ const void* q_row_ptr(const void* Q, int esize, const ScoreArgs& a,
-                                                 int l, int g, int B, int b, int r, int D) {
+                                                 int l, int g, int b, int r) {
   const int hl = r / a.W, w = r - hl * a.W;
   const int h = g * a.G + hl;
-  const int64_t row = ((int64_t)l * a.Hq + h) * ((int64_t)B * a.W) + (int64_t)b * a.W + w;
-  return (const char*)Q + row * D * esize;
+  const int64_t off = (int64_t)l * a.qsl + (int64_t)h * a.qsh + ((int64_t)b * a.W + w) * a.qsr;
+  return (const char*)Q + off * esize;
+}
+
+// First token of sequence b of KV head lh (= l * Hkv + g); token i at + i * kst.
+template <typename T>
+__device__ __forceinline__ const T* k_head(const T* K, const ScoreArgs& a, const SeqTable& st,
+                                           int lh, int b) {
+  const int l = lh / a.Hkv, g = lh - l * a.Hkv;
+  return K + (int64_t)l * a.ksl + (int64_t)g * a.ksh + st.cu[b] * a.kst;
 }
 
 // --------------------------------------------------------------------------
@@ -167,7 +178,7 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[2][D / 16], const __bf
   for (int qt = 0; qt < 2; ++qt) {
     const int r = rg * 64 + qt * 32 + (lane & 31);
     if (r < a.M) {
-      const __bf16* qr = (const __bf16*)q_row_ptr(Q, 2, a, l, g, st.B, b, r, D);
+      const __bf16* qr = (const __bf16*)q_row_ptr(Q, 2, a, l, g, b, r);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qf[qt][kk] = *(const bf16x8*)(qr + kk * 16 + col8);
     } else {
@@ -206,11 +217,11 @@ __device__ __forceinline__ int wave_min_limit(const ScoreArgs& a, int N, int rg,
 // last valid key instead (always in bounds, no per-lane branch); callers
 // mask them.
 template <int D>
-__device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[D / 16], const __bf16* Kh, int64_t key,
-                                             int64_t key_end, int lane) {
+__device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[D / 16], const __bf16* Kh, int64_t kst,
+                                             int64_t key, int64_t key_end, int lane) {
   const int col8 = (lane >> 5) * 8;
   const int64_t row = key < key_end ? key : key_end - 1;
-  const __bf16* kr = Kh + row * D;
+  const __bf16* kr = Kh + row * kst;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *(const bf16x8*)(kr + kk * 16 + col8);
 }
@@ -341,19 +352,19 @@ __device__ __forceinline__ void tile_row_stats(const bf16x8 (&qf)[2][D / 16],
 // stay exact; scheduling barriers keep the loads ahead of the arithmetic.
 // The tile count is uniform, so the loop runs on scalar control.
 template <int D, int STEP, typename F>
-__device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t first, int64_t end,
-                                            int lane, F&& body) {
+__device__ __forceinline__ void sweep_tiles(const __bf16* Kh, int64_t kst, int64_t first,
+                                            int64_t end, int lane, F&& body) {
   const int ntile = __builtin_amdgcn_readfirstlane(
       first < end ? (int)((end - first + STEP - 1) / STEP) : 0);
   if (ntile == 0) return;
   bf16x8 ka[D / 16], kb[D / 16];
-  load_k_frags<D>(ka, Kh, first + (lane & 31), end, lane);
+  load_k_frags<D>(ka, Kh, kst, first + (lane & 31), end, lane);
   for (int it = 0; it < ntile; it += 2) {
     const int64_t key0 = first + (int64_t)it * STEP;
-    load_k_frags<D>(kb, Kh, key0 + STEP + (lane & 31), end, lane);
+    load_k_frags<D>(kb, Kh, kst, key0 + STEP + (lane & 31), end, lane);
     __builtin_amdgcn_sched_barrier(0);
     body(ka, key0);
-    load_k_frags<D>(ka, Kh, key0 + 2 * STEP + (lane & 31), end, lane);
+    load_k_frags<D>(ka, Kh, kst, key0 + 2 * STEP + (lane & 31), end, lane);
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < ntile) body(kb, key0 + STEP);
   }
@@ -446,7 +457,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
   const int N = (int)st.N[b];
   const int64_t key_begin = (int64_t)c * a.chunk;
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
-  const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
+  const __bf16* Kh = k_head(K, a, st, lh, b);
 
   static_assert(NRG == 1, "several row groups use score_pass_shared");
 
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
       else
         tile_row_stats<D, true>(qf, kf, a.c2, (int)key0, lim, lane, m, s);
     };
-    sweep_tiles<D, STEP>(Kh, key_begin + kg * 32, key_end, lane, body1);
+    sweep_tiles<D, STEP>(Kh, a.kst, key_begin + kg * 32, key_end, lane, body1);
     // lanes l and l + 32 hold the same rows over different keys
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -531,7 +542,7 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
         cv += __shfl_xor(cv, 32);
         if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
       };
-      sweep_tiles<D, STEP>(Kh, sub0 + kg * 32, sub1, lane, body2);
+      sweep_tiles<D, STEP>(Kh, a.kst, sub0 + kg * 32, sub1, lane, body2);
       __syncthreads();
       for (int i = tid; i < sub1 - sub0; i += TH) {
         float v = cs[0][i];
@@ -590,7 +601,7 @@ __global__ __launch_bounds__(64 * NRG, 2) void score_pass_shared(
   const int N = (int)st.N[b];
   const int64_t key_begin = (int64_t)c * a.chunk;
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
-  const __bf16* Kh = K + ((int64_t)lh * a.T + st.cu[b]) * D;
+  const __bf16* Kh = k_head(K, a, st, lh, b);
   const int nst = __builtin_amdgcn_readfirstlane((int)((key_end - key_begin + SK - 1) / SK));
 
   // wave w's tile of the stage at s0 into buffer `buf`; rows past the end
@@ -603,7 +614,7 @@ __global__ __launch_bounds__(64 * NRG, 2) void score_pass_shared(
       const int piece = dslot ^ (r & (PPR - 1));
       int64_t key = s0 + 32 * wave + r;
       key = key < key_end ? key : key_end - 1;
-      __builtin_amdgcn_global_load_lds((gvoid_p)(Kh + key * D + piece * 8),
+      __builtin_amdgcn_global_load_lds((gvoid_p)(Kh + key * a.kst + piece * 8),
                                        (lvoid_p)(kbuf[buf] + wave * TILEB + i * 1024), 16, 0,
                                        0);
     }
@@ -737,7 +748,7 @@ __global__ __launch_bounds__(256) void score_stats_f32(const float* __restrict__
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
   const bool have = key < key_end;
   float kr[D];
-  const float* kp = K + ((int64_t)lh * a.T + st.cu[b] + (have ? key : key_begin)) * D;
+  const float* kp = k_head(K, a, st, lh, b) + (have ? key : key_begin) * a.kst;
 #pragma unroll
   for (int e = 0; e < D; ++e) kr[e] = kp[e];
   for (int r0 = 0; r0 < a.M; r0 += 16) {
@@ -745,7 +756,7 @@ __global__ __launch_bounds__(256) void score_stats_f32(const float* __restrict__
     for (int i = tid; i < 16 * D; i += 256) {
       const int rr = r0 + i / D;
       qs[i / D][i % D] =
-          rr < a.M ? ((const float*)q_row_ptr(Q, 4, a, l, g, st.B, b, rr, D))[i % D] : 0.f;
+          rr < a.M ? ((const float*)q_row_ptr(Q, 4, a, l, g, b, rr))[i % D] : 0.f;
     }
     __syncthreads();
     const int rend = min(16, a.M - r0);
@@ -798,7 +809,7 @@ __global__ __launch_bounds__(256) void score_probs_f32(const float* __restrict__
   const int64_t key_end = key_begin + a.chunk < N ? key_begin + a.chunk : N;
   const bool have = key < key_end;
   float kr[D];
-  const float* kp = K + ((int64_t)lh * a.T + st.cu[b] + (have ? key : key_begin)) * D;
+  const float* kp = k_head(K, a, st, lh, b) + (have ? key : key_begin) * a.kst;
 #pragma unroll
   for (int e = 0; e < D; ++e) kr[e] = kp[e];
   const float* rs = rowstat + ((int64_t)lh * st.B + b) * a.Mpad;
@@ -808,7 +819,7 @@ __global__ __launch_bounds__(256) void score_probs_f32(const float* __restrict__
     for (int i = tid; i < 16 * D; i += 256) {
       const int rr = r0 + i / D;
       qs[i / D][i % D] =
-          rr < a.M ? ((const float*)q_row_ptr(Q, 4, a, l, g, st.B, b, rr, D))[i % D] : 0.f;
+          rr < a.M ? ((const float*)q_row_ptr(Q, 4, a, l, g, b, rr))[i % D] : 0.f;
     }
     if (tid < 16) ms[tid] = r0 + tid < a.M ? rs[r0 + tid] : INFINITY;
     __syncthreads();
@@ -960,8 +971,9 @@ hipError_t dispatch_mfma(const void* q, const void* k, const SeqTable& st, const
 }  // namespace
 
 hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable& st, int L, int Hq,
-                        int Hkv, int W, int d, float scale, int causal, float* s,
-                        double* head_stats, char* ws, const ScoreGeom& geo, hipStream_t stream) {
+                        int Hkv, int W, int d, const ScoreStrides& sd, float scale, int causal,
+                        float* s, double* head_stats, char* ws, const ScoreGeom& geo,
+                        hipStream_t stream) {
   ScoreArgs a{};
   a.L = L;
   a.Hq = Hq;
@@ -975,6 +987,12 @@ hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable&
   a.causal = causal ? 1 : 0;
   a.T = 0;
   for (int b = 0; b < st.B; ++b) a.T += st.N[b];
+  a.qsl = sd.q_l;
+  a.qsh = sd.q_h;
+  a.qsr = sd.q_r;
+  a.ksl = sd.k_l;
+  a.ksh = sd.k_h;
+  a.kst = sd.k_t;
   a.c2 = (float)((double)scale * 1.4426950408889634);
   if (dtype == 1)
     return d == 128 ? dispatch_mfma<128>(q, k, st, a, ws, geo, s, head_stats, stream)
