@@ -157,7 +157,8 @@ def bench_decode(args, w):
                 if evs is not None:
                     evs[t - t0][0].record(stream)
                 hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t, w.scale, w.n_sink, w.recent,
-                            bool(w.include_self), evicted=ev, out=o, stream=stream)
+                            bool(w.include_self), evicted=ev, out=o, stream=stream,
+                            ring=args.ring)
                 if evs is not None:
                     evs[t - t0][1].record(stream)
                 t += 1
@@ -172,7 +173,7 @@ def bench_decode(args, w):
     t0 = time.perf_counter()
     for i in range(steps):
         hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, out=o, stream=stream)
+                    bool(w.include_self), evicted=ev, out=o, stream=stream, ring=args.ring)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     t += steps
@@ -184,7 +185,7 @@ def bench_decode(args, w):
     for i in range(steps):
         evs[i][0].record(stream)
         hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, out=o, stream=stream)
+                    bool(w.include_self), evicted=ev, out=o, stream=stream, ring=args.ring)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     t += steps
@@ -233,7 +234,9 @@ def bench_decode(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "heavy": w.heavy,
                    "recent": w.recent, "prompt_steps_untimed": w.prompt,
-                   "attention_output": o is not None, "parallelism": "none (1 GPU)"},
+                   "attention_output": o is not None,
+                   "slot_layout": "ring" if args.ring else "fixed",
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": "h2o_step",
                      "kernels": "h2o_step_kernel", "algorithmic_bytes": nbytes},
@@ -313,6 +316,8 @@ def main(argv=None):
                     help="planted-burst coverage diagnostic instead of the benchmark")
     ap.add_argument("--attn-out", action="store_true",
                     help="decode workload: h2o_step also writes the attention output")
+    ap.add_argument("--ring", action="store_true",
+                    help="decode workload: the recent window in a ring of slots (h2o_step_ring)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "

@@ -13,6 +13,7 @@
  *                  a layer's budget shared by its KV heads (per-head floors)
  *   hubkv_nestedkv a second base score from the keys alone (NestedKV)
  *   h2o_step       one streaming (decode) step of H2O greedy eviction
+ *   h2o_step_ring  the same step with the recent window kept in a ring of slots
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE memory unless the parameter says "host".
@@ -306,6 +307,30 @@ int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, voi
              int Hq, int Hkv, int d, int C, int n_sink, int n_recent, float scale,
              int include_self, int32_t* evicted /* nullable */, float* probs /* nullable */,
              float* out /* nullable */, void* stream);
+
+/*
+ * h2o_step_ring -- h2o_step on the ring slot layout of the H2O breakdown
+ * page's FlexGen section (the recent region is a circular queue of slots
+ * whose head and tail advance in O(1)).  Slots [0, C - n_recent) hold heavy
+ * tokens; slots [C - n_recent, C) are the ring, and position p sits in ring
+ * slot C - n_recent + p mod n_recent.  The new token t[b] takes the ring slot
+ * of position t[b] - n_recent, the token that leaves the recent window; that
+ * token moves (K/V row, acc, pos copied) to the lowest free heavy slot, or,
+ * with the heavy slots full, the token with the smallest acc among the heavy
+ * positions in [n_sink, t - n_recent] and the leaving token itself is
+ * evicted (ties to the oldest position); when the victim is a heavy token,
+ * the leaving token takes its slot.  The candidates are the fixed layout's,
+ * so a cache driven by this call from empty, with t advancing by one per
+ * step, retains the same tokens with the same acc as h2o_step (in other
+ * slots; probs follow this layout's slots).  Arguments, outputs and limits
+ * as for h2o_step, plus 1 <= n_recent < C.  A cache must be driven by one
+ * layout from empty.
+ */
+int h2o_step_ring(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+                  void* v_cache, float* acc, int32_t* pos, const int64_t* t /* host [B] */, int B,
+                  int Hq, int Hkv, int d, int C, int n_sink, int n_recent, float scale,
+                  int include_self, int32_t* evicted /* nullable */, float* probs /* nullable */,
+                  float* out /* nullable */, void* stream);
 
 /* Number of protected positions of a sequence of length N (host helper). */
 int64_t hubkv_protected_count(int64_t N, int n_sink, int n_recent);

@@ -251,3 +251,21 @@ def test_compact_strided_validation():
     assert call(ki=P + 8, ks=[0, 0, d]) == EALIGN            # inputs may overlap (reads only)
     # nothing is kept: no output row is addressed and nothing is launched
     assert call(kept=(0,), os_=[0, 0, 0], vos=[0, 0, 0]) == 0
+
+
+def test_h2o_step_ring_validation():
+    L = hk.lib()
+
+    def call(C_=64, ns=0, nr=8, acc=P):
+        return L.h2o_step_ring(P, P, P, 1, P, P, acc, P, a64([100]), 1, 4, 4, 128, C_, ns, nr,
+                               0.1, 0, None, None, None, None)
+
+    # valid layouts reach the alignment check (the last one before a launch)
+    assert call(acc=P + 2) == EALIGN
+    assert call(C_=64, nr=63, acc=P + 2) == EALIGN   # one heavy slot
+    assert call(nr=0) == EINVAL                      # no ring
+    assert call(C_=8, nr=8) == EINVAL                # no heavy slot
+    assert call(ns=60, nr=8) == EINVAL               # protected windows exceed the capacity
+    # the fixed-slot call keeps accepting n_recent = 0 and n_recent = C
+    assert L.h2o_step(P, P, P, 1, P, P, P + 2, P, a64([100]), 1, 4, 4, 128, 8, 0, 8, 0.1, 0,
+                      None, None, None, None) == EALIGN

@@ -18,6 +18,7 @@ Functions (names follow the C ABI):
     hubkv_select_layer(z, seqlens, layer_kept, ...)    -> (idx, head_kept)
     hubkv_compact_layer(k, v, idx, head_kept, seqlens, layer_kept) -> (k_out, v_out)
     h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, ...) -> evicted
+    (ring=True: h2o_step_ring, the recent window in a ring of slots)
 """
 from __future__ import annotations
 
@@ -71,6 +72,8 @@ _SIGS = {
                             _sz, _vp]),
     "h2o_step": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, _i, _f,
                       _i, _vp, _vp, _vp, _vp]),
+    "h2o_step_ring": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i64p, _i, _i, _i, _i, _i, _i, _i,
+                           _f, _i, _vp, _vp, _vp, _vp]),
     "hubkv_protected_count": (_i64, [_i64, _i, _i]),
     "hubkv_strerror": (C.c_char_p, [_i]),
     "hubkv_last_hip_error": (_i, []),
@@ -333,12 +336,13 @@ def hubkv_compact_layer(k_in, v_in, idx, head_kept, seqlens: Sequence[int], laye
 
 def h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, scale: float, n_sink: int = 0,
              n_recent: int = 0, include_self: bool = False, evicted=None, probs=None,
-             out=None, stream=None):
+             out=None, stream=None, ring: bool = False):
     """One H2O decode step, in place on (k_cache, v_cache, acc, pos).
     q [B][Hq][d], k_new/v_new [B][Hkv][d], caches [B][Hkv][C][d], acc/pos
     [B][Hkv][C]; t: int or per-sequence list.  probs (fp32 [B][Hq][C+1]) and
     out (fp32 [B][Hq][d], the attention output) are filled when given.
-    Returns evicted int32 [B][Hkv]."""
+    ring=True keeps the recent window in a ring of the last n_recent slots
+    (h2o_step_ring).  Returns evicted int32 [B][Hkv]."""
     torch = _torch()
     B, Hq, d = q.shape
     _, Hkv, Cs, _ = k_cache.shape
@@ -348,7 +352,8 @@ def h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, scale: float, n_sin
     for name, x, shape in (("probs", probs, (B, Hq, Cs + 1)), ("out", out, (B, Hq, d))):
         if x is not None and (x.dtype != torch.float32 or tuple(x.shape) != shape):
             raise ValueError(f"{name} must be float32 of shape {shape}")
-    _check("h2o_step", lib().h2o_step(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q),
+    name = "h2o_step_ring" if ring else "h2o_step"
+    _check(name, getattr(lib(), name)(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q),
                                       _ptr(k_cache), _ptr(v_cache), _ptr(acc), _ptr(pos),
                                       _arr64(tt), B, Hq, Hkv, d, Cs, int(n_sink), int(n_recent),
                                       float(scale), int(bool(include_self)), _ptr(evicted),

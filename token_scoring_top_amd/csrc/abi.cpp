@@ -477,16 +477,19 @@ int hubkv_nestedkv(const void* k, int dtype, int B, const int64_t* seqlens, int 
                                     (hipStream_t)stream));
 }
 
-int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+namespace {
+
+int h2o_impl(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
              void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
              int d, int C, int n_sink, int n_recent, float scale, int include_self,
-             int32_t* evicted, float* probs, float* out, void* stream) {
+             int32_t* evicted, float* probs, float* out, void* stream, int ring) {
   int rc = check_dtype_d(dtype, d);
   if (rc) return rc;
   if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
   const int G = Hq / Hkv;
   if (G > 16 || C < 1 || (int64_t)(G + 1) * C > 16384) return HUBKV_EINVAL;
   if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > C) return HUBKV_EINVAL;
+  if (ring && (n_recent < 1 || n_recent >= C)) return HUBKV_EINVAL;  // a ring and a heavy slot
   if ((int64_t)B * Hkv > ((int64_t)1 << 30) || !isfinite(scale)) return HUBKV_EINVAL;
   H2OArgs a;
   memset(&a, 0, sizeof(a));
@@ -509,9 +512,28 @@ int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, voi
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   a.include_self = include_self ? 1 : 0;
+  a.ring = ring;
   a.scale = scale;
   return hip_status(launch_h2o_step(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, a, evicted,
                                     probs, out, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+             void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
+             int d, int C, int n_sink, int n_recent, float scale, int include_self,
+             int32_t* evicted, float* probs, float* out, void* stream) {
+  return h2o_impl(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, t, B, Hq, Hkv, d, C, n_sink,
+                  n_recent, scale, include_self, evicted, probs, out, stream, 0);
+}
+
+int h2o_step_ring(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+                  void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq,
+                  int Hkv, int d, int C, int n_sink, int n_recent, float scale, int include_self,
+                  int32_t* evicted, float* probs, float* out, void* stream) {
+  return h2o_impl(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, t, B, Hq, Hkv, d, C, n_sink,
+                  n_recent, scale, include_self, evicted, probs, out, stream, 1);
 }
 
 }  // extern "C"

@@ -23,6 +23,19 @@
 // the partial sums are folded across the lanes of a wave with shuffles and
 // across waves in LDS, in a fixed order.  The sweep reads the cache before the
 // new token's row is written into its slot.
+//
+// Ring layout (H2O breakdown page, FlexGen section: the recent region is a
+// circular queue whose head and tail advance in O(1)): slots [0, C - R) hold
+// the heavy tokens and slots [C - R, C) a ring of R = n_recent slots, where
+// position p always sits in slot C - R + p mod R.  The new token t takes the
+// ring slot of t - R, the token leaving the recent window.  That token moves
+// to a free heavy slot if there is one; otherwise the lowest (score,
+// position) among the heavy candidates and the leaving token is evicted, and
+// when the victim is a heavy token the leaving token's row, score and
+// position are copied into the victim's slot (one extra row copy).  The
+// candidates are those of the fixed layout (positions in [n_sink,
+// t - n_recent]), so both layouts retain the same tokens with the same scores
+// when t advances by one per step.
 #include "internal.hpp"
 
 namespace hubkv {
@@ -80,8 +93,8 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   __shared__ float Mh[KG], iLh[KG], selfx[KG], pself[KG];
   __shared__ unsigned long long cand_key[WAVES];
   __shared__ int cand_slot[WAVES], empty_w[WAVES];
-  __shared__ int dec_slot;
-  __shared__ float dec_acc;
+  __shared__ int dec_slot, dec_move, dec_mpos;
+  __shared__ float dec_acc, dec_macc, ring_acc;
 
   const int u = blockIdx.x;
   const int b = u / a.Hkv, g = u % a.Hkv;
@@ -224,8 +237,11 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   // the first V rows are in flight during the score update
   if (out) load_v(wave * RPWV, vnx);
 
-  // ---- score update, eviction candidate, first empty slot
+  // ---- score update, eviction candidate, first empty slot (a heavy slot in
+  // the ring layout)
   const int64_t lo = a.n_sink, hi = t - a.n_recent;
+  const int nheavy = a.ring ? C - a.n_recent : C;
+  const int rslot = a.ring ? nheavy + (int)(t % a.n_recent) : -1;  // the new token's ring slot
   unsigned long long best = ~0ull;
   int best_slot = -1, first_empty = 0x7fffffff;
   for (int j = tid; j < C; j += kH2OThreads) {
@@ -238,10 +254,11 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       if (probs) probs[((int64_t)b * a.Hq + g * G + h) * (C + 1) + j] = p;
     }
     if (pj < 0) {
-      first_empty = min(first_empty, j);
+      if (j < nheavy) first_empty = min(first_empty, j);
     } else {
       const float na = A[j] + add;
       A[j] = na;
+      if (j == rslot) ring_acc = na;
       if (pj >= lo && pj <= hi) {
         const unsigned long long key = ((unsigned long long)asc_key(na) << 32) | (uint32_t)pj;
         if (key < best) {
@@ -285,8 +302,24 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       }
       fe = min(fe, empty_w[w]);
     }
-    int slot = -1, ev = -1;
-    if (fe < C) {
+    int slot = -1, ev = -1, mv = -1;
+    if (a.ring) {
+      // the new token takes its ring slot; the token leaving it moves to a
+      // free heavy slot, or the lowest candidate (it included) is evicted
+      const int32_t pold = pl[rslot];
+      if (pold < 0) {
+        slot = rslot;
+      } else if (fe < nheavy) {
+        slot = rslot;
+        mv = fe;
+      } else if (bs >= 0) {
+        slot = rslot;
+        ev = (int)(bk & 0xffffffffu);
+        if (bs != rslot) mv = bs;
+      }
+      dec_mpos = pold;
+      dec_macc = ring_acc;
+    } else if (fe < C) {
       slot = fe;
     } else {
       // the new token competes when it is outside both protected windows
@@ -305,6 +338,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       }
     }
     dec_slot = slot;
+    dec_move = mv;
     dec_acc = self_acc;  // 0 unless the new token attends to itself
     if (evicted) evicted[u] = ev;
   }
@@ -364,10 +398,14 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     }
   }
 
-  const int slot = dec_slot;
+  const int slot = dec_slot, mv = dec_move;
+  // a slot's owner thread rewrites its score and position (it wrote the
+  // updated score above, so program order keeps the final value)
+  if (mv >= 0 && (mv % kH2OThreads) == tid) {
+    A[mv] = dec_macc;
+    pos[(int64_t)u * C + mv] = dec_mpos;
+  }
   if (slot >= 0) {
-    // the slot's owner thread rewrites its score and position (it wrote the
-    // updated score above, so program order keeps the final value)
     if ((slot % kH2OThreads) == tid) {
       A[slot] = dec_acc;
       pos[(int64_t)u * C + slot] = (int32_t)t;
@@ -375,6 +413,15 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     if (wave == 0 && lane < LPR) {
       const int64_t src = ((int64_t)b * a.Hkv + g) * D + lane * EPL;
       const int64_t dst = ((int64_t)u * C + slot) * D + lane * EPL;
+      if (mv >= 0) {
+        // the leaving token's row goes to its heavy slot before the new row
+        // overwrites it (same lane, same addresses: program order holds)
+        const int64_t mdst = ((int64_t)u * C + mv) * D + lane * EPL;
+        const u32x4 kr = *(const u32x4*)(k_cache + dst);
+        const u32x4 vr = *(const u32x4*)(v_cache + dst);
+        *(u32x4*)(k_cache + mdst) = kr;
+        *(u32x4*)(v_cache + mdst) = vr;
+      }
       *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_new + src);
       *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_new + src);
     }

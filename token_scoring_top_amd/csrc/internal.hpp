@@ -169,6 +169,7 @@ hipError_t launch_compact(const void* k_in, const void* v_in, int elem_bytes, co
 // ---- streaming H2O step ------------------------------------------------------------
 struct H2OArgs {
   int B, Hq, Hkv, d, C, n_sink, n_recent, include_self;
+  int ring;  // 0: fixed slots; 1: heavy slots [0, C - n_recent) + a ring of n_recent slots
   float scale;
   int64_t t[kMaxSeqs];
 };
