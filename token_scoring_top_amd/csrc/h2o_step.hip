@@ -151,20 +151,22 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       const bool occ = j < C && pl[j] >= 0;
 #pragma unroll
       for (int h = 0; h < KG; ++h) {
-        if (h >= G) break;
-        float d = 0.f;
+        if (h < G) {  // G is uniform: every lane takes the same branch
+          float d = 0.f;
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
+          for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
-        const float x2 = occ ? d * c2 : -INFINITY;
-        if (piece == 0 && j < C) {
-          lg[h * C + j] = x2;
-          // running softmax statistics of this lane's slots
-          if (x2 > -INFINITY) {
-            const float mn = fmaxf(om[h], x2);
-            os[h] = os[h] * __builtin_amdgcn_exp2f(om[h] - mn) + __builtin_amdgcn_exp2f(x2 - mn);
-            om[h] = mn;
+          for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+          const float x2 = occ ? d * c2 : -INFINITY;
+          if (piece == 0 && j < C) {
+            lg[h * C + j] = x2;
+            // running softmax statistics of this lane's slots
+            if (x2 > -INFINITY) {
+              const float mn = fmaxf(om[h], x2);
+              os[h] = os[h] * __builtin_amdgcn_exp2f(om[h] - mn) +
+                      __builtin_amdgcn_exp2f(x2 - mn);
+              om[h] = mn;
+            }
           }
         }
       }
@@ -185,20 +187,21 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   // ---- softmax statistics per query head: merge the lanes' running (m, s)
 #pragma unroll
   for (int h = 0; h < KG; ++h) {
-    if (h >= G) break;
-    float m = om[h], sm = os[h];
+    if (h < G) {  // G is uniform: every lane takes the same branch
+      float m = om[h], sm = os[h];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
-      const float mn = fmaxf(m, m2);
-      if (mn > -INFINITY) {
-        sm = sm * __builtin_amdgcn_exp2f(m - mn) + s2 * __builtin_amdgcn_exp2f(m2 - mn);
-        m = mn;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sm, off);
+        const float mn = fmaxf(m, m2);
+        if (mn > -INFINITY) {
+          sm = sm * __builtin_amdgcn_exp2f(m - mn) + s2 * __builtin_amdgcn_exp2f(m2 - mn);
+          m = mn;
+        }
       }
-    }
-    if (lane == 0) {
-      red[wave][h] = m;
-      red2[wave][h] = sm;
+      if (lane == 0) {
+        red[wave][h] = m;
+        red2[wave][h] = sm;
+      }
     }
   }
   __syncthreads();
@@ -367,10 +370,11 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
           for (int x = 0; x < EPLV; ++x) vv[x] = to_f<T>(e[x]);
 #pragma unroll
           for (int h = 0; h < KG; ++h) {
-            if (h >= G) break;
-            const float p = lg[h * C + j];
+            if (h < G) {  // G is uniform: every lane takes the same branch
+              const float p = lg[h * C + j];
 #pragma unroll
-            for (int x = 0; x < EPLV; ++x) o[h][x] = fmaf(p, vv[x], o[h][x]);
+              for (int x = 0; x < EPLV; ++x) o[h][x] = fmaf(p, vv[x], o[h][x]);
+            }
           }
         }
       }
@@ -378,13 +382,14 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     // fold the rows of a wave, then park the wave's sums in LDS
 #pragma unroll
     for (int h = 0; h < KG; ++h) {
-      if (h >= G) break;
+      if (h < G) {  // G is uniform: every lane takes the same branch
 #pragma unroll
-      for (int x = 0; x < EPLV; ++x) {
-        float v = o[h][x];
+        for (int x = 0; x < EPLV; ++x) {
+          float v = o[h][x];
 #pragma unroll
-        for (int off = LPRV; off < 64; off <<= 1) v += __shfl_xor(v, off);
-        if (rv == 0) part[(wave * G + h) * D + pv * EPLV + x] = v;
+          for (int off = LPRV; off < 64; off <<= 1) v += __shfl_xor(v, off);
+          if (rv == 0) part[(wave * G + h) * D + pv * EPLV + x] = v;
+        }
       }
     }
     __syncthreads();  // every wave's V reads are done before the slot rewrite below

@@ -236,7 +236,8 @@ __global__ __launch_bounds__(kT) void nkv_anomaly(const T* __restrict__ K, NkvAr
   const int64_t t1 = t0 + kNkvAnTile < N ? t0 + kNkvAnTile : N;
   const int64_t row_base = (int64_t)lh * a.T + a.cu[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* bsum = (const float*)(ws + g.off_bsum) + ((int64_t)lh * a.nblk_total + a.blk_off[b]) * D;
+  const float* bsum =
+      (const float*)(ws + g.off_bsum) + ((int64_t)lh * a.nblk_total + a.blk_off[b]) * D;
   const float* bnrm = (const float*)(ws + g.off_bnorm) + (int64_t)lh * a.nblk_total + a.blk_off[b];
   const float* invn = (const float*)(ws + g.off_inv) + row_base;
   // the sequence sum (block sums in order) and its norm

@@ -228,7 +228,9 @@ __device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[D / 16], const __bf16*
 
 // Output element j of a 32x32 tile sits at row 8 (j / 4) + 4 (lane / 32) +
 // (j % 4) and column lane % 32.
-__device__ __forceinline__ int c_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+__device__ __forceinline__ int c_row(int j, int lane) {
+  return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+}
 
 // Column sums of one 32-key tile over the wave's 64 query rows: logits of
 // both 32-row query tiles on v_mfma_f32_32x32x16_bf16 (queries as rows, this
@@ -793,7 +795,8 @@ __global__ __launch_bounds__(256) void score_stats_f32(const float* __restrict__
 template <int D>
 __global__ __launch_bounds__(256) void score_probs_f32(const float* __restrict__ Q,
                                                        const float* __restrict__ K, SeqTable st,
-                                                       ScoreArgs a, const float* __restrict__ rowstat,
+                                                       ScoreArgs a,
+                                                       const float* __restrict__ rowstat,
                                                        float* __restrict__ s_out,
                                                        double2* __restrict__ part2) {
   __shared__ float qs[16][D];
@@ -873,7 +876,8 @@ __global__ __launch_bounds__(256) void score_combine(SeqTable st, ScoreArgs a,
   for (int c = c0; c < c1; c += 8) {
     float2 p[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = c + u < c1 ? pp[(int64_t)(c + u) * a.Mpad] : make_float2(kMinit, 0.f);
+    for (int u = 0; u < 8; ++u)
+      p[u] = c + u < c1 ? pp[(int64_t)(c + u) * a.Mpad] : make_float2(kMinit, 0.f);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (p[u].y > 0.f) merge_ml(m, s, p[u].x, p[u].y);

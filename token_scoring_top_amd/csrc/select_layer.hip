@@ -50,7 +50,9 @@ __device__ __forceinline__ uint32_t ordkey(float v) {
   return v != v ? 0u : k;
 }
 
-__device__ __forceinline__ constexpr int lv_shift(int lv) { return lv == 0 ? 21 : (lv == 1 ? 10 : 0); }
+__device__ __forceinline__ constexpr int lv_shift(int lv) {
+  return lv == 0 ? 21 : (lv == 1 ? 10 : 0);
+}
 __device__ __forceinline__ constexpr int lv_bits(int lv) { return lv == 2 ? 10 : 11; }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -151,7 +153,8 @@ __device__ __forceinline__ Chunk chunk_of(const LselArgs& a, const float* z) {
 // The chunk's keys: thread t holds positions p0 + t + kT j; kNone marks a
 // protected position or one past the chunk (kNone is above every order key
 // and is never counted as a candidate).
-__device__ __forceinline__ void load_keys(const LselArgs& a, const Chunk& k, uint32_t (&key)[kPer]) {
+__device__ __forceinline__ void load_keys(const LselArgs& a, const Chunk& k,
+                                          uint32_t (&key)[kPer]) {
   const int64_t lo = a.n_sink, hi = k.N - a.n_recent;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -378,8 +381,9 @@ __global__ __launch_bounds__(kT) void lsel_pool_level(const float* __restrict__ 
 
 // ---- pool keys above / at tau per head; the last work-group of a (layer,
 // sequence) sets every head's kept count, emission threshold and offset
-__global__ __launch_bounds__(kT) void lsel_count(const float* __restrict__ z, LselArgs a, LselGeom g,
-                                                 char* base, int32_t* __restrict__ head_kept) {
+__global__ __launch_bounds__(kT) void lsel_count(const float* __restrict__ z, LselArgs a,
+                                                 LselGeom g, char* base,
+                                                 int32_t* __restrict__ head_kept) {
   __shared__ uint32_t rg[kT / 64], re[kT / 64], flag;
   const Ws w = ws_of(base, g);
   const Chunk k = chunk_of(a, z);
