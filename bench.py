@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "1eeaeb0410b0c04530eea87172224065d37a60aed16debe62d708a83d2a78ed3", "workload": 2,
-                 "fetch_bytes": 546600386, "write_bytes": 4350851}
+SCORE_TRAFFIC = {"sha256": "c0b40caba94144381e323bbd281a7871614b5d9eb7951d590fb11d36c54cd60e", "workload": 2,
+                 "fetch_bytes": 546601367, "write_bytes": 4350912}
 
 
 def _score_source_sha() -> str:
