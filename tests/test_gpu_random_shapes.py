@@ -10,7 +10,11 @@ Each case draws, from its own seed:
 - for the score: d 64 or 128, G * W up to 512, bf16 or fp32, causal or not;
 - for the decode step: a drawn mid-stream cache of 2 to 500 slots, partly
   empty or full, group sizes 1 to 8, with or without the new token attending
-  to itself.
+  to itself;
+- for the ring slot layout of the decode step: 2 to 100 slots, streamed from
+  empty past the capacity;
+- for the score and the compaction: packed, token-major or padded views of
+  Q, K, V and of the compaction outputs (strided calls).
 
 The bars are those of the dedicated tests:
 - integer and bit results (refined scores, kept sets, compaction, the
@@ -21,7 +25,9 @@ The bars are those of the dedicated tests:
   inputs) or 2e-2 (bf16), the attention output within 1e-5 / 1e-4 of the
   scale of its terms. The evicted slot is identical unless the oracle's two
   best candidates lie within 1e-4, and where it is identical, the slots
-  (positions, K and V rows) are bit-exact.
+  (positions, K and V rows) are bit-exact;
+- strided calls return the packed calls' bits; the ring layout retains the
+  oracle's positions, scores and rows.
 """
 import math
 
@@ -72,6 +78,23 @@ def _windows(rng, seqlens):
     return ns, nr
 
 
+def _view(rng, x):
+    """x itself, or the same values in a token-major or padded layout (a
+    non-contiguous view of x's shape with a contiguous last axis)."""
+    kind = str(rng.choice(["packed", "token-major", "padded"]))
+    if kind == "token-major":
+        return kind, x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    if kind == "padded":
+        L, H, R, d = x.shape
+        per = 16 // x.element_size()
+        buf = torch.zeros((L, H, R + int(rng.integers(0, 40)), d + per * int(rng.integers(1, 4))),
+                          dtype=x.dtype, device=x.device)
+        v = buf[:, :, :R, :d]
+        v.copy_(x)
+        return kind, v
+    return kind, x
+
+
 def _kept(rng, seqlens, ns, nr):
     out = []
     for n in seqlens:
@@ -107,11 +130,21 @@ def test_refine_select_compact(seed):
     d = 64
     K = S.round_bf16(rng.standard_normal((L, Hkv, sum(seqlens), d), dtype=np.float32))
     V = S.round_bf16(rng.standard_normal((L, Hkv, sum(seqlens), d), dtype=np.float32))
-    ko, vo = hk.hubkv_compact(to_dev(K, "bf16"), to_dev(V, "bf16"), idx_g, seqlens, kept)
+    Kd, Vd = to_dev(K, "bf16"), to_dev(V, "bf16")
+    ko, vo = hk.hubkv_compact(Kd, Vd, idx_g, seqlens, kept)
+    # the same through strided views of the inputs and of the outputs
+    kk, kv = _view(rng, Kd)
+    vk, vv = _view(rng, Vd)
+    Kt = int(sum(kept))
+    ok_, ko_s = _view(rng, torch.zeros((L, Hkv, Kt, d), dtype=torch.bfloat16, device="cuda"))
+    ov_, vo_s = _view(rng, torch.zeros((L, Hkv, Kt, d), dtype=torch.bfloat16, device="cuda"))
+    note(f"  compaction views: {kk} {vk} -> {ok_} {ov_}")
+    hk.hubkv_compact(kv, vv, idx_g, seqlens, kept, k_out=ko_s, v_out=vo_s)
     torch.cuda.synchronize()
     ko_o, vo_o = oracle.compact(K, V, idx_o, seqlens, kept)
     np.testing.assert_array_equal(to_host(ko), ko_o)
     np.testing.assert_array_equal(to_host(vo), vo_o)
+    assert torch.equal(ko_s, ko) and torch.equal(vo_s, vo)
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -162,11 +195,18 @@ def test_score(seed):
     scale = 1 / math.sqrt(d)
     note(f"  {dtype} d={d} Hq={Hq} Hkv={Hkv} W={W} seqlens={seqlens} L={L} causal={causal}")
     s_o, st_o = oracle.score(Q, K, seqlens, W, scale, causal)
-    s_g, st_g = hk.hubkv_score(to_dev(Q, dtype), to_dev(K, dtype), seqlens, W, scale, causal)
+    Qd, Kd = to_dev(Q, dtype), to_dev(K, dtype)
+    s_g, st_g = hk.hubkv_score(Qd, Kd, seqlens, W, scale, causal)
+    # the same through strided views: identical bits
+    qk, qv = _view(rng, Qd)
+    kk, kv = _view(rng, Kd)
+    note(f"  views: q {qk}, k {kk}")
+    s_v, st_v = hk.hubkv_score(qv, kv, seqlens, W, scale, causal)
     torch.cuda.synchronize()
     tol = 5e-5 if dtype == "bf16" else 1e-5
     assert rel_err(s_g.cpu().numpy(), s_o, 1e-30).max() < tol
     np.testing.assert_allclose(st_g.cpu().numpy()[..., 0], st_o[..., 0], rtol=1e-5)
+    assert torch.equal(s_v, s_g) and torch.equal(st_v, st_g)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -247,3 +287,58 @@ def test_h2o_step(seed):
                 pr_o[b, hq, -1] * np.abs(st["v_new"][b, g].astype(np.float64))
             err = np.abs(o_g[b, hq] - o_o[b, hq]) / np.maximum(scale, 1e-30)
             assert err.max() < (1e-5 if dtype == "f32" else 1e-4), err.max()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_h2o_ring_stream(seed):
+    """h2o_step_ring from an empty cache for C + 10..80 steps beside the
+    oracle's fixed slots: the same evictions (near-ties aside), and at the end
+    the same retained positions, scores and K/V rows."""
+    rng = np.random.default_rng(6000 + seed)
+    dtype = str(rng.choice(["bf16", "f32"]))
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4]))
+    Hkv, B = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    heavy, recent = int(rng.integers(1, 61)), int(rng.integers(1, 41))
+    C = heavy + recent
+    n_sink = int(rng.integers(0, min(heavy, 5) + 1))
+    inc = int(rng.integers(0, 2))
+    steps = C + int(rng.integers(10, 81))
+    w = S.workload(4).with_(B=B, Hkv=Hkv, Hq=G * Hkv, d=d, heavy=heavy, recent=recent,
+                            dtype=dtype, n_sink=n_sink)
+    note(f"  {dtype} d={d} B={B} Hkv={Hkv} G={G} heavy={heavy} recent={recent} "
+         f"sink={n_sink} self={inc} steps={steps}")
+    q = rng.standard_normal((steps, B, G * Hkv, d), dtype=np.float32)
+    k = rng.standard_normal((steps, B, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((steps, B, Hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = S.round_bf16(q), S.round_bf16(k), S.round_bf16(v)
+    st_o = oracle.empty_state(B, Hkv, C, d)
+    ds = {"K": to_dev(st_o["K"], dtype), "V": to_dev(st_o["V"], dtype),
+          "acc": torch.from_numpy(st_o["acc"].copy()).cuda(),
+          "pos": torch.from_numpy(st_o["pos"].copy()).cuda()}
+    diverged = np.zeros((B, Hkv), bool)
+    for t in range(steps):
+        ev_g = hk.h2o_step(to_dev(q[t], dtype), to_dev(k[t], dtype), to_dev(v[t], dtype),
+                           ds["K"], ds["V"], ds["acc"], ds["pos"], t, w.scale, n_sink, recent,
+                           inc, ring=True)
+        ev_o, mg = oracle.h2o_step(st_o, q[t], k[t], v[t], t, w.scale, n_sink, recent, inc,
+                                   want_margin=True)
+        newly = (ev_g.cpu().numpy() != ev_o) & ~diverged
+        assert np.all(mg[newly] <= 1e-4), f"step {t}: divergence without a near-tie"
+        diverged |= newly
+    pos_g, acc_g = ds["pos"].cpu().numpy(), ds["acc"].cpu().numpy()
+    K_g, V_g = to_host(ds["K"]), to_host(ds["V"])
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for b in range(B):
+        for g in range(Hkv):
+            if diverged[b, g]:
+                continue
+            og = np.argsort(np.where(pos_g[b, g] >= 0, pos_g[b, g], np.iinfo(np.int32).max))
+            oo = np.argsort(np.where(st_o["pos"][b, g] >= 0, st_o["pos"][b, g],
+                                     np.iinfo(np.int32).max))
+            np.testing.assert_array_equal(pos_g[b, g][og], st_o["pos"][b, g][oo])
+            live = st_o["pos"][b, g][oo] >= 0
+            assert rel_err(acc_g[b, g][og][live], st_o["acc"][b, g][oo][live], 1e-30).max() < tol
+            np.testing.assert_array_equal(K_g[b, g][og][live], st_o["K"][b, g][oo][live])
+            np.testing.assert_array_equal(V_g[b, g][og][live], st_o["V"][b, g][oo][live])
