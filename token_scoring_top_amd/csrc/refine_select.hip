@@ -403,6 +403,24 @@ __device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool 
                                            int32_t* __restrict__ out) {
   uint32_t thw = thr;
   asm volatile("" : "+v"(thw));  // keeps earlier compares against thr from being reused
+  // usual case: no key of the wave's rows equals thr, so the tie count Tt
+  // stays put and each row needs one ballot
+  bool anyeq = false;
+#pragma unroll
+  for (int j = 0; j < kSelKpt; ++j) anyeq |= key[j] == thw;
+  if (!__any(anyeq)) {
+    uint32_t base = D + (Tt < rem ? Tt : rem);
+#pragma unroll
+    for (int j = 0; j < kSelKpt; ++j) {
+      const uint32_t k = key[j];
+      const bool def = edge ? (k > thw && k != kPad) : (k > thw);
+      const unsigned long long bd = __ballot(def);
+      const uint32_t o = base + rank_below(bd);
+      if (def && o < (uint32_t)kept) out[o] = p0 + 64 * j;
+      base += (uint32_t)__popcll(bd);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kSelKpt; ++j) {
     const uint32_t k = key[j];
