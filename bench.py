@@ -316,6 +316,8 @@ def main(argv=None):
                     help="planted-burst coverage diagnostic instead of the benchmark")
     ap.add_argument("--attn-out", action="store_true",
                     help="decode workload: h2o_step also writes the attention output")
+    ap.add_argument("--graph", action="store_true",
+                    help="prefill: time replays of one step captured into a HIP graph")
     ap.add_argument("--ring", action="store_true",
                     help="decode workload: the recent window in a ring of slots (h2o_step_ring)")
     args = ap.parse_args(argv)
@@ -404,9 +406,10 @@ def main(argv=None):
                        dtype=torch.uint8, device="cuda")
     ws_r = torch.empty(max(256, hk.lib().hubkv_refine_workspace(w.B, sl, L, Hkv)),
                        dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
+    launch_stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, strm=None):
+        stream = strm if strm is not None else launch_stream
         if ev: ev[0].record(stream)
         if args.nestedkv:
             # key-only score: no queries, no refinement (the scores are not
@@ -437,11 +440,26 @@ def main(argv=None):
 
     for _ in range(args.warmup):
         step()
+    graph = None
+    if args.graph:
+        # one step captured into a HIP graph (every buffer is preallocated and
+        # the library allocates nothing, so the capture holds only kernels)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(launch_stream)
+        with torch.cuda.graph(graph, stream=cap):
+            step(strm=cap)
+        launch_stream.wait_stream(cap)
+        for _ in range(args.warmup):
+            graph.replay()
     # timed region: whole steps back to back, no markers between the ops
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -572,6 +590,7 @@ def main(argv=None):
                    "scorer": "nestedkv" if args.nestedkv else "attention-mass",
                    "head_floor": floor if args.layer_budget else None,
                    "zipf_mass": zipf,
+                   "launch": "hip graph replay of one step" if args.graph else "eager",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "op": dom,
