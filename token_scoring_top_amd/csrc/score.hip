@@ -427,9 +427,23 @@ __device__ __forceinline__ void finish_chunk_stats(double hs, double ha, double2
       // the unit's last chunk: head statistics, chunks added in order
       double S2 = 0.0, A2 = 0.0;
       const double* p2 = (const double*)(part2 + (int64_t)lh * a.nchunk + st.tile_off[b]);
-      for (int cc = 0; cc < nch; ++cc) {
-        S2 += ld_agent(p2 + 2 * cc);
-        A2 += ld_agent(p2 + 2 * cc + 1);
+      // eight chunks' loads in flight at a time (clamped, always in bounds),
+      // then added in chunk order
+      for (int c0 = 0; c0 < nch; c0 += 8) {
+        double sv[8], av[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int cc = c0 + e < nch ? c0 + e : nch - 1;
+          sv[e] = ld_agent(p2 + 2 * cc);
+          av[e] = ld_agent(p2 + 2 * cc + 1);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (c0 + e < nch) {
+            S2 += sv[e];
+            A2 += av[e];
+          }
+        }
       }
       const int64_t su = (((int64_t)l * st.B + b) * a.Hkv + g) * 2;
       stats[su] = S2;
