@@ -525,9 +525,9 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
   } else {
     // ---- pass 2: queries as MFMA rows, keys as columns: lane l owns key
     // key0 + l % 32 and 16 rows of each query tile, so a column sum is a
-    // lane-local sum plus one exchange between the two half-waves.
-    constexpr int kSub = 8192;  // one round per 4096-key chunk
-    __shared__ float cs[NRG][kSub];
+    // lane-local sum plus one exchange between the two half-waves.  With one
+    // row group that sum is final: the low half-wave stores it at once and
+    // keeps its chunk statistics in registers (no LDS pass, no barrier).
     __shared__ double2 hred[WAVES];
     // row normalisers in LDS: a lane's 16 rows of a query tile are 4 runs of
     // 4 consecutive rows, the same for every lane of a half-wave, so they are
@@ -539,37 +539,28 @@ __global__ __launch_bounds__(64 * NRG * NKG, 2) void score_pass_mfma(
     __syncthreads();
     double hs = 0.0, ha = 0.0;
     float* so = s_out + (int64_t)lh * a.T + st.cu[b];
-    for (int64_t sub0 = key_begin; sub0 < key_end; sub0 += kSub) {
-      const int64_t sub1 = sub0 + kSub < key_end ? sub0 + kSub : key_end;
-      const int last = (int)sub1 - 1;
-      const int minlim = wave_min_limit(a, N, rg, lane, last);
-      auto body2 = [&](const bf16x8 (&kf)[KS], int64_t key0) {
-        const int key = (int)key0 + (lane & 31);
-        // fully visible tiles (nearly all) and masked ones get separate
-        // straight-line copies, so the scheduler can overlap the second MFMA
-        // chain with the first chain's exponentials
-        float cv;
-        if ((int)key0 + 31 <= minlim)
-          cv = tile_col_sums<D, false>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
-                                       last);
-        else
-          cv = tile_col_sums<D, true>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
-                                      last);
-        cv += __shfl_xor(cv, 32);
-        if (lane < 32) cs[rg][(int)(key0 - sub0) + lane] = cv;
-      };
-      sweep_tiles<D, STEP>(Kh, a.kst, sub0 + kg * 32, sub1, lane, body2);
-      __syncthreads();
-      for (int i = tid; i < sub1 - sub0; i += TH) {
-        float v = cs[0][i];
-#pragma unroll
-        for (int q = 1; q < NRG; ++q) v += cs[q][i];
-        so[sub0 + i] = v;
-        hs += (double)v;
-        if (v > 0.f) ha += (double)v * (double)(__builtin_amdgcn_logf(v) * kLn2);
+    const int last = (int)key_end - 1;
+    const int minlim = wave_min_limit(a, N, rg, lane, last);
+    auto body2 = [&](const bf16x8 (&kf)[KS], int64_t key0) {
+      const int key = (int)key0 + (lane & 31);
+      // fully visible tiles (nearly all) and masked ones get separate
+      // straight-line copies, so the scheduler can overlap the second MFMA
+      // chain with the first chain's exponentials
+      float cv;
+      if ((int)key0 + 31 <= minlim)
+        cv = tile_col_sums<D, false>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                     last);
+      else
+        cv = tile_col_sums<D, true>(qf, kf, mrow + rg * 64, rlim + rg * 64, a.c2, lane, key,
+                                    last);
+      cv += __shfl_xor(cv, 32);
+      if (lane < 32 && key <= last) {
+        so[key] = cv;
+        hs += (double)cv;
+        if (cv > 0.f) ha += (double)cv * (double)(__builtin_amdgcn_logf(cv) * kLn2);
       }
-      __syncthreads();
-    }
+    };
+    sweep_tiles<D, STEP>(Kh, a.kst, key_begin + kg * 32, key_end, lane, body2);
     finish_chunk_stats<WAVES>(hs, ha, hred, part2, ctl + u, a, st, lh, chunk_g, b, nch, l, g,
                               stats, tid, lane, wave);
   }
