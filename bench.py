@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "c0b40caba94144381e323bbd281a7871614b5d9eb7951d590fb11d36c54cd60e", "workload": 2,
-                 "fetch_bytes": 546601367, "write_bytes": 4350912}
+SCORE_TRAFFIC = {"sha256": "8c1eca34354a8732b72584a8fec191ad327bb4c7ce077b92855dc8d6646ac2a6", "workload": 2,
+                 "fetch_bytes": 546608317, "write_bytes": 4350993}
 
 
 def _score_source_sha() -> str:
