@@ -30,6 +30,23 @@ def test_library_exports_every_declared_function():
     assert L.hubkv_version() >= 100
 
 
+def test_library_exports_nothing_else():
+    """Every global function symbol of the library is one the header declares
+    (internal helpers have internal linkage)."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", hk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines()
+                if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    ours = {n for n in exported if n.startswith(("hubkv", "h2o"))}
+    assert ours == set(hk.header_functions()) & ours
+    assert ours >= {n for n in hk.header_functions() if n.startswith(("hubkv", "h2o"))}
+    assert not {n for n in exported if not n.startswith("_")} - ours
+
+
 def test_strerror_and_last_error():
     L = hk.lib()
     for code in (0, -1, -2, -3, -4, -5):

@@ -200,6 +200,50 @@ int make_nkv(NkvArgs& a, int B, const int64_t* seqlens, int L, int Hkv, int d, i
 
 }  // namespace
 
+namespace {
+
+// Shared body of h2o_step (ring = 0) and h2o_step_ring (ring = 1).
+int h2o_impl(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
+             void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
+             int d, int C, int n_sink, int n_recent, float scale, int include_self,
+             int32_t* evicted, float* probs, float* out, void* stream, int ring) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
+  const int G = Hq / Hkv;
+  if (G > 16 || C < 1 || (int64_t)(G + 1) * C > 16384) return HUBKV_EINVAL;
+  if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > C) return HUBKV_EINVAL;
+  if (ring && (n_recent < 1 || n_recent >= C)) return HUBKV_EINVAL;  // a ring and a heavy slot
+  if ((int64_t)B * Hkv > ((int64_t)1 << 30) || !isfinite(scale)) return HUBKV_EINVAL;
+  H2OArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int b = 0; b < B; ++b) {
+    if (t[b] < 0 || t[b] >= kMaxTokens - 1) return HUBKV_EINVAL;
+    a.t[b] = t[b];
+  }
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !acc || !pos) return HUBKV_EALIGN;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(acc, 4) || !aligned(pos, 4))
+    return HUBKV_EALIGN;
+  if ((evicted && !aligned(evicted, 4)) || (probs && !aligned(probs, 4)) ||
+      (out && !aligned(out, 4)))
+    return HUBKV_EALIGN;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.C = C;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.include_self = include_self ? 1 : 0;
+  a.ring = ring;
+  a.scale = scale;
+  return hip_status(launch_h2o_step(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, a, evicted,
+                                    probs, out, (hipStream_t)stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 int64_t hubkv_protected_count(int64_t N, int n_sink, int n_recent) {
@@ -477,48 +521,6 @@ int hubkv_nestedkv(const void* k, int dtype, int B, const int64_t* seqlens, int 
                                     (hipStream_t)stream));
 }
 
-namespace {
-
-int h2o_impl(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
-             void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
-             int d, int C, int n_sink, int n_recent, float scale, int include_self,
-             int32_t* evicted, float* probs, float* out, void* stream, int ring) {
-  int rc = check_dtype_d(dtype, d);
-  if (rc) return rc;
-  if (B < 1 || B > kMaxSeqs || Hq < 1 || Hkv < 1 || Hq % Hkv || !t) return HUBKV_EINVAL;
-  const int G = Hq / Hkv;
-  if (G > 16 || C < 1 || (int64_t)(G + 1) * C > 16384) return HUBKV_EINVAL;
-  if (n_sink < 0 || n_recent < 0 || (int64_t)n_sink + n_recent > C) return HUBKV_EINVAL;
-  if (ring && (n_recent < 1 || n_recent >= C)) return HUBKV_EINVAL;  // a ring and a heavy slot
-  if ((int64_t)B * Hkv > ((int64_t)1 << 30) || !isfinite(scale)) return HUBKV_EINVAL;
-  H2OArgs a;
-  memset(&a, 0, sizeof(a));
-  for (int b = 0; b < B; ++b) {
-    if (t[b] < 0 || t[b] >= kMaxTokens - 1) return HUBKV_EINVAL;
-    a.t[b] = t[b];
-  }
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !acc || !pos) return HUBKV_EALIGN;
-  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
-      !aligned(v_cache, 16) || !aligned(acc, 4) || !aligned(pos, 4))
-    return HUBKV_EALIGN;
-  if ((evicted && !aligned(evicted, 4)) || (probs && !aligned(probs, 4)) ||
-      (out && !aligned(out, 4)))
-    return HUBKV_EALIGN;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.d = d;
-  a.C = C;
-  a.n_sink = n_sink;
-  a.n_recent = n_recent;
-  a.include_self = include_self ? 1 : 0;
-  a.ring = ring;
-  a.scale = scale;
-  return hip_status(launch_h2o_step(q, k_new, v_new, dtype, k_cache, v_cache, acc, pos, a, evicted,
-                                    probs, out, (hipStream_t)stream));
-}
-
-}  // namespace
 
 int h2o_step(const void* q, const void* k_new, const void* v_new, int dtype, void* k_cache,
              void* v_cache, float* acc, int32_t* pos, const int64_t* t, int B, int Hq, int Hkv,
