@@ -40,13 +40,25 @@ SCORE_TRAFFIC = {"sha256": "8c1eca34354a8732b72584a8fec191ad327bb4c7ce077b92855d
                  "fetch_bytes": 546608317, "write_bytes": 4350993}
 
 
-def _score_source_sha() -> str:
+# The same for one full-cache h2o_step launch of the decode workload (scores
+# only, fixed slots), from `bench.py --workload 4 --steps 8 --warmup 1
+# --no-cpu-baseline` (the last 1000 launches).  Valid only for the decode
+# source it was taken on.
+DECODE_TRAFFIC = {"sha256": "af5eb02272d454f36ae5a41f5beed47461383c1c1d7d1bc0f043c28f94020c45", "workload": 4,
+                  "fetch_bytes": 554208249, "write_bytes": 8683520}
+
+
+def _source_sha(files) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("score.hip", "internal.hpp"):
+    for f in files:
         with open(os.path.join(ROOT, "token_scoring_top_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def _score_source_sha() -> str:
+    return _source_sha(("score.hip", "internal.hpp"))
 
 
 def copy_calibration(reps: int = 5) -> int:
@@ -192,6 +204,10 @@ def bench_decode(args, w):
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     nbytes = h2o_step_bytes(w, elem, o is not None)
     ach = nbytes / (k_ms / 1e3) / 1e9
+    dec_traffic = None
+    if (o is None and not args.ring and DECODE_TRAFFIC["workload"] == w.wid
+            and DECODE_TRAFFIC["sha256"] == _source_sha(("h2o_step.hip", "internal.hpp"))):
+        dec_traffic = DECODE_TRAFFIC["fetch_bytes"] + DECODE_TRAFFIC["write_bytes"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -238,7 +254,7 @@ def bench_decode(args, w):
                    "slot_layout": "ring" if args.ring else "fixed",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "op": "h2o_step",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": dec_traffic, "op": "h2o_step",
                      "kernels": "h2o_step_kernel", "algorithmic_bytes": nbytes},
         "kernel_ms": k_ms,
         "cpu_baseline": cpu,
