@@ -1,0 +1,15 @@
+"""Host-side check of bench.py's contract (no GPU needed): it runs on one GPU
+only, and says so when asked for more."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
