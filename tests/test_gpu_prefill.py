@@ -165,6 +165,8 @@ SELECT_CASES = [
     ([200], 1, 1, 1.0, 4, 32, "attention"),           # keep everything
     ([100], 1, 1, 0.5, 60, 60, "attention"),          # windows overlap: all protected
     ([262144], 1, 1, 0.2, 4, 128, "ties"),
+    ([600001], 1, 1, 0.1, 4, 128, "attention"),       # past 16 rounds: the general path
+    ([540000, 7], 1, 1, 0.05, 0, 64, "special"),      # general path, long, NaN / signs / inf
 ]
 
 
