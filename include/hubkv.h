@@ -50,7 +50,9 @@
  * K and V.  Each stride is a non-negative multiple of 16 bytes; an output
  * view must not map two (layer, head, row) triples onto the same bytes.
  *
- * Limits: 1 <= B <= 64; d in {64, 128}; Hq % Hkv == 0; (Hq/Hkv)*W <= 512;
+ * Limits: 1 <= B <= 64; 1 <= every sequence length < 2^30 (positions and
+ * their rounding to tiles are int32 in the kernels; longer sequences return
+ * HUBKV_EINVAL); d in {64, 128}; Hq % Hkv == 0; (Hq/Hkv)*W <= 512;
  * W <= every sequence length; element type HUBKV_F32 or HUBKV_BF16; Q/K/V
  * base pointers 16-byte aligned, fp32/int32 arrays 4-byte aligned, fp64
  * arrays 8-byte aligned.

@@ -286,3 +286,25 @@ def test_h2o_step_ring_validation():
     # the fixed-slot call keeps accepting n_recent = 0 and n_recent = C
     assert L.h2o_step(P, P, P, 1, P, P, P + 2, P, a64([100]), 1, 4, 4, 128, 8, 0, 8, 0.1, 0,
                       None, None, None, None) == EALIGN
+
+
+def test_sequence_length_limit():
+    """Every entry point rejects a sequence of 2^30 tokens or more on the host:
+    the kernels round positions up to whole tiles and select rounds in int32."""
+    L = hk.lib()
+    for n in ((1 << 30), (1 << 31) - 10, (1 << 31) - 1):
+        sl = a64([n])
+        kept = a64([n // 2])
+        assert L.hubkv_select(P, 1, sl, 1, 1, kept, 0, 0, P, None) == EINVAL
+        assert L.hubkv_refine(P, 1, sl, 1, 1, None, None, 5, 0.5, 0.8, 1.2, 0.1, P + (1 << 40),
+                              None, P, 1 << 40, None) == EINVAL
+        assert L.hubkv_compact(P, P, 1, P, 1, sl, kept, 1, 1, 128, P, P, None) == EINVAL
+        assert L.hubkv_score(P, P, 1, 1, sl, 1, 1, 1, 16, 128, 0.1, 1, P, None, P, 1 << 40,
+                             None) == EINVAL
+        assert L.hubkv_score_workspace(1, sl, 1, 1, 1, 16, 128, 1) == 0
+        assert L.hubkv_refine_workspace(1, sl, 1, 1) == 0
+        assert L.hubkv_select_layer_workspace(1, sl, 1, 1) == 0
+        assert L.hubkv_nestedkv_workspace(1, sl, 1, 1, 128, 32) == 0
+    # one below the limit passes the length check
+    sl = a64([(1 << 30) - 1])
+    assert L.hubkv_refine_workspace(1, sl, 1, 1) > 0

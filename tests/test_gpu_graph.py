@@ -45,20 +45,29 @@ def test_prefill_chain_graph_replays_match_eager(G, W):
     Kd = torch.empty((L, Hkv, T, d), dtype=torch.bfloat16, **dev)
     Vd = torch.empty_like(Kd)
 
+    def poison(o):
+        # every element a replay or an eager chain leaves unwritten stays a
+        # sentinel (NaN or -2^31) and fails the comparisons below
+        for v in o.values():
+            v.fill_(float("nan") if v.is_floating_point() else -(1 << 31))
+        return o
+
     def outputs():
-        return dict(s=torch.empty((L, Hkv, T), dtype=torch.float32, **dev),
+        return poison(dict(s=torch.empty((L, Hkv, T), dtype=torch.float32, **dev),
                     st=torch.empty((L, len(seqlens), Hkv, 2), dtype=torch.float64, **dev),
                     z=torch.empty((L, Hkv, T), dtype=torch.float32, **dev),
                     beta=torch.empty((L, len(seqlens), Hkv), dtype=torch.float32, **dev),
                     idx=torch.empty((L, Hkv, Ksum), dtype=torch.int32, **dev),
                     ko=torch.empty((L, Hkv, Ksum, d), dtype=torch.bfloat16, **dev),
-                    vo=torch.empty((L, Hkv, Ksum, d), dtype=torch.bfloat16, **dev))
+                    vo=torch.empty((L, Hkv, Ksum, d), dtype=torch.bfloat16, **dev)))
 
     sl = hk._arr64(seqlens)
     ws_s = torch.empty(hk.lib().hubkv_score_workspace(len(seqlens), sl, L, Hq, Hkv, W, d, 1),
                        dtype=torch.uint8, **dev)
     ws_r = torch.empty(max(256, hk.lib().hubkv_refine_workspace(len(seqlens), sl, L, Hkv)),
                        dtype=torch.uint8, **dev)
+    ws_s.fill_(255)
+    ws_r.fill_(255)
 
     def chain(o, strm):
         hk.hubkv_score(Qd, Kd, seqlens, W, scale, True, s=o["s"], head_stats=o["st"],
@@ -89,6 +98,9 @@ def test_prefill_chain_graph_replays_match_eager(G, W):
     other = outputs()
     for rep in range(4):
         draw(100 + rep)
+        poison(og)
+        poison(oe)
+        torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         got = {k: v.clone() for k, v in og.items()}

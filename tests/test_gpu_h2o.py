@@ -54,7 +54,7 @@ def _dev_state(st, dtype):
 
 def _gpu_step(ds, q, kn, vn, t, w, n_sink, n_recent, include_self, dtype, want_probs=True):
     B, Hq = q.shape[0], q.shape[1]
-    probs = torch.zeros((B, Hq, w.C + 1), dtype=torch.float32, device="cuda") if want_probs else None
+    probs = torch.full((B, Hq, w.C + 1), float("nan"), device="cuda") if want_probs else None
     ev = hk.h2o_step(to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), ds["K"], ds["V"],
                      ds["acc"], ds["pos"], t, w.scale, n_sink, n_recent, include_self, probs=probs)
     torch.cuda.synchronize()
@@ -63,7 +63,7 @@ def _gpu_step(ds, q, kn, vn, t, w, n_sink, n_recent, include_self, dtype, want_p
 
 def _gpu_step_out(ds, q, kn, vn, t, w, n_sink, n_recent, include_self, dtype):
     B, Hq, d = q.shape
-    probs = torch.zeros((B, Hq, w.C + 1), dtype=torch.float32, device="cuda")
+    probs = torch.full((B, Hq, w.C + 1), float("nan"), device="cuda")
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     ev = hk.h2o_step(to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), ds["K"], ds["V"],
                      ds["acc"], ds["pos"], t, w.scale, n_sink, n_recent, include_self,

@@ -91,7 +91,7 @@ def test_ring_stream_matches_oracle(case):
     for t in range(steps):
         pos_g0 = ds["pos"].cpu().numpy()
         pos_o0, V_o0 = st_o["pos"].copy(), st_o["V"].copy()
-        probs = torch.zeros((B, Hq, Cs + 1), dtype=torch.float32, device="cuda")
+        probs = torch.full((B, Hq, Cs + 1), float("nan"), device="cuda")
         out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda") \
             if want_out else None
         ev_g = hk.h2o_step(to_dev(q[t], dtype), to_dev(k[t], dtype), to_dev(v[t], dtype),

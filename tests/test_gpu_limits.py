@@ -106,7 +106,7 @@ def test_decode_step_at_64_sequences():
     ds = {"K": to_dev(st["K"], "bf16"), "V": to_dev(st["V"], "bf16"),
           "acc": torch.from_numpy(st["acc"].copy()).cuda(),
           "pos": torch.from_numpy(st["pos"].copy()).cuda()}
-    probs = torch.zeros((w.B, w.Hq, w.C + 1), dtype=torch.float32, device="cuda")
+    probs = torch.full((w.B, w.Hq, w.C + 1), float("nan"), device="cuda")
     ev_g = hk.h2o_step(to_dev(st["q"], "bf16"), to_dev(st["k_new"], "bf16"),
                        to_dev(st["v_new"], "bf16"), ds["K"], ds["V"], ds["acc"], ds["pos"], t,
                        w.scale, w.n_sink, w.recent, 0, probs=probs)

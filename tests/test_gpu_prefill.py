@@ -165,22 +165,60 @@ SELECT_CASES = [
     ([200], 1, 1, 1.0, 4, 32, "attention"),           # keep everything
     ([100], 1, 1, 0.5, 60, 60, "attention"),          # windows overlap: all protected
     ([262144], 1, 1, 0.2, 4, 128, "ties"),
+    ([491520], 1, 2, 0.1, 4, 128, "ties"),            # 15 rounds of 32768, fast path
+    ([524288], 1, 2, 0.1, 4, 128, "attention"),       # exactly 16 rounds: the fast path's last
+    ([524288], 1, 1, 0.05, 4, 128, "ties"),
+    ([524288], 1, 1, None, 4, 128, "bin8192"),        # threshold bin of exactly 8192 keys (LDS cap)
+    ([524288], 1, 1, None, 4, 128, "bin8193"),        # one key over the cap: the general path
+    ([491520, 4099], 1, 1, None, 0, 64, "bin8000"),   # a planted bin just under the cap, ragged
     ([600001], 1, 1, 0.1, 4, 128, "attention"),       # past 16 rounds: the general path
     ([540000, 7], 1, 1, 0.05, 0, 64, "special"),      # general path, long, NaN / signs / inf
 ]
 
 
+def _planted_bin_z(seqlens, n_bin, seed, ns, nr):
+    """Scores in [1, 2) (raw bits 0x3f800000 .. 0x3fffffff, both ends present
+    among the unprotected keys of the first sequence) with n_bin keys planted
+    in [1.5, 1.5 + 4096 ulp) and every other key outside it; kept counts put
+    the k-th largest unprotected key inside the planted run (which holds many
+    ties).  With that range the select's first pass bins 4096 ulps at a time,
+    so the planted run is exactly one bin."""
+    rng = np.random.default_rng(seed)
+    lo, hi, c0 = 0x3F800000, 0x3FFFFFFF, 0x3FC00000
+    zs, kept = [], []
+    for b, n in enumerate(seqlens):
+        bits = rng.integers(lo, hi + 1, n, dtype=np.int64)
+        inbin = (bits >= c0) & (bits < c0 + 4096)
+        bits[inbin] += 4096
+        a = min(ns, n)
+        c = max(n - nr, a)
+        cand = np.arange(a, c)
+        nb = n_bin if b == 0 else min(n_bin, cand.size // 4)
+        pick = rng.choice(cand, nb + 2, replace=False)
+        bits[pick[:nb]] = c0 + rng.integers(0, 4096, nb)
+        bits[pick[nb]], bits[pick[nb + 1]] = lo, hi
+        above = int(np.count_nonzero(bits[cand] >= c0 + 4096))
+        kept.append(above + nb // 2 + (n - cand.size))
+        zs.append(bits.astype(np.uint32).view(np.float32))
+    return np.concatenate(zs)[None, None], np.array(kept, np.int64)
+
+
 @pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: f"T{sum(c[0])}-{c[6]}-b{c[3]}")
 def test_select_bitexact_given_scores(case):
     seqlens, L, Hkv, budget, ns, nr, kind = case
-    if kind == "special":
+    kept = None
+    if kind.startswith("bin"):
+        z, kept = _planted_bin_z(seqlens, int(kind[3:]), sum(seqlens), ns, nr)
+    elif kind == "special":
         z = np.stack([np.stack([_special_z(sum(seqlens), 10 * l + h) for h in range(Hkv)])
                       for l in range(L)])
     else:
         z = S.random_scores(seqlens, L, Hkv, seed=len(seqlens) + sum(seqlens),
                             kind="uniform" if kind == "uniform" else "attention",
                             ties=(kind == "ties"))
-    if budget is None:
+    if kept is not None:
+        pass
+    elif budget is None:
         kept = np.array([oracle.protected_count(n, ns, nr) for n in seqlens])
     else:
         kept = np.maximum(S.budgets(seqlens, budget),
@@ -286,17 +324,28 @@ def test_chain_gqa_long_context_two_layers():
     assert (g["beta"][1] >= np.float32(0.8)).all() and (g["beta"][1] <= np.float32(1.2)).all()
 
 
+_C5 = {}
+
+
+def _ragged_inputs():
+    """Inputs of the ragged workload (4 sequences, 983040 tokens, 8 KV heads),
+    drawn once per test process."""
+    if "w" not in _C5:
+        w = S.workload(5)
+        note("  generating 4 sequences (983040 tokens) x 8 heads")
+        _C5["w"] = w
+        _C5["qkv"] = S.prefill_inputs(w, threads=threads())
+    return _C5["w"], _C5["qkv"]
+
+
 @pytest.mark.parametrize("budget", [0.05, 0.1, 0.2])
 def test_chain_ragged_batch_at_scale(budget):
-    # 4 sequences of 64K..512K tokens on the GPU; the oracle checks the 64K
-    # sequence in full (its 8 heads), the rest by invariants
-    w = S.workload(5).with_(budget=budget, r=budget)
-    key = "c5"
-    cache = test_chain_ragged_batch_at_scale.__dict__
-    if key not in cache:
-        note("  generating 4 sequences (983040 tokens) x 8 heads")
-        cache[key] = S.prefill_inputs(w, threads=threads())
-    Q, K, V = cache[key]
+    # 4 sequences of 64K..512K tokens on the GPU.  The oracle runs the whole
+    # chain on the 64K sequence (its 8 heads); for every sequence it refines
+    # the GPU's own scores with the GPU's head weights, selects from the GPU's
+    # own refined scores and gathers the rows, and those must match bit for bit
+    w0_, (Q, K, V) = _ragged_inputs()
+    w = w0_.with_(budget=budget, r=budget)
     g = _gpu_chain(Q, K, V, w)
     w0 = w.with_(seqlens=(w.seqlens[0],))
     n0 = w.seqlens[0]
@@ -308,14 +357,52 @@ def test_chain_ragged_batch_at_scale(budget):
               k_out=g["k_out"][:, :, :k0], v_out=g["v_out"][:, :, :k0], kept=g["kept"][:1])
     _check_chain(g0, o, K[:, :, :n0], V[:, :, :n0], w0, tol_s=2e-2, tol_set=2e-2)
     assert rel_err(g0["s"], o["s"]).max() < 5e-5
-    # every sequence: column sums, kept counts, ascending, protected windows
+    # every sequence, from the GPU's own fp32 scores
+    note("  oracle refine / select / compaction of all four sequences on the GPU's scores")
+    st_o = oracle.head_stats(g["s"], w.seqlens)
+    np.testing.assert_allclose(g["stats"][..., 0], st_o[..., 0], rtol=1e-6)
+    np.testing.assert_allclose(g["stats"][..., 1], st_o[..., 1], rtol=1e-5)
+    b_o = oracle.beta(g["stats"], w.seqlens, w.beta_lo, w.beta_hi)
+    assert rel_err(g["beta"], b_o).max() < 1e-6
+    z_o = oracle.refine(g["s"], w.seqlens, g["beta"], w.pool, w.gamma, w.r)
+    np.testing.assert_array_equal(g["z"], z_o)
+    idx_o = oracle.select(g["z"], w.seqlens, g["kept"], w.n_sink, w.n_recent)
+    np.testing.assert_array_equal(g["idx"], idx_o)
+    ko, vo = oracle.compact(K, V, idx_o, w.seqlens, g["kept"])
+    np.testing.assert_array_equal(g["k_out"], ko)
+    np.testing.assert_array_equal(g["v_out"], vo)
+    # and the invariants of every sequence's scores
     cu = np.concatenate([[0], np.cumsum(w.seqlens)])
-    ko = np.concatenate([[0], np.cumsum(g["kept"])])
     for b, N in enumerate(w.seqlens):
         np.testing.assert_allclose(g["s"][0, :, cu[b]:cu[b + 1]].astype(np.float64).sum(-1),
                                    w.G * w.W, rtol=1e-4)
-        for h in range(w.Hkv):
-            x = g["idx"][0, h, ko[b]:ko[b + 1]]
-            assert (np.diff(x) > 0).all() and x[0] == 0 and x[-1] == N - 1
-            assert set(range(w.n_sink)) <= set(x[:w.n_sink + 1].tolist())
-            assert (x[-w.n_recent:] == np.arange(N - w.n_recent, N)).all()
+
+
+def test_score_ragged_long_sequences_one_head():
+    """Scores of the 262144- and 524288-token sequences (93% of the ragged
+    workload with the 131072 one), one KV head, element by element.  The
+    oracle scores each of the group's query heads as its own unit (the KV
+    head's keys repeated) and the four score arrays are added in float64:
+    s is the sum over the group's heads, so this is the same quantity."""
+    w, (Q, K, V) = _ragged_inputs()
+    g = 5
+    s_g, st_g = _gpu_score(Q, K, w.seqlens, w.W, w.scale, w.causal, "bf16")
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)])
+    bs = [2, 3]
+    lens = [w.seqlens[b] for b in bs]
+    G = w.G
+    Qg = np.ascontiguousarray(np.concatenate(
+        [Q[:, g * G:(g + 1) * G, b * w.W:(b + 1) * w.W] for b in bs], axis=2))
+    Kg = np.concatenate([K[:, g, cu[b]:cu[b + 1]] for b in bs], axis=1)   # [1][T'][d]
+    Kg = np.ascontiguousarray(np.broadcast_to(Kg[:, None], (1, G) + Kg.shape[1:]))
+    note(f"  oracle score of KV head {g} on sequences of {lens} tokens ({G} query heads)")
+    s_o, _ = oracle.score(Qg, Kg, lens, w.W, w.scale, w.causal)
+    s_o = s_o.astype(np.float64).sum(axis=1)[0]
+    o = 0
+    for b, N in zip(bs, lens):
+        got = s_g[0, g, cu[b]:cu[b + 1]]
+        ref = s_o[o:o + N]
+        o += N
+        err = rel_err(got, ref)
+        assert err.max() < 2e-2
+        assert err.max() < 5e-5, f"sequence {b}: max rel err {err.max():.3g}"

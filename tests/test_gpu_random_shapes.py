@@ -136,8 +136,10 @@ def test_refine_select_compact(seed):
     kk, kv = _view(rng, Kd)
     vk, vv = _view(rng, Vd)
     Kt = int(sum(kept))
-    ok_, ko_s = _view(rng, torch.zeros((L, Hkv, Kt, d), dtype=torch.bfloat16, device="cuda"))
-    ov_, vo_s = _view(rng, torch.zeros((L, Hkv, Kt, d), dtype=torch.bfloat16, device="cuda"))
+    ok_, ko_s = _view(rng, torch.full((L, Hkv, Kt, d), float("nan"), dtype=torch.bfloat16,
+                                      device="cuda"))
+    ov_, vo_s = _view(rng, torch.full((L, Hkv, Kt, d), float("nan"), dtype=torch.bfloat16,
+                                      device="cuda"))
     note(f"  compaction views: {kk} {vk} -> {ok_} {ov_}")
     hk.hubkv_compact(kv, vv, idx_g, seqlens, kept, k_out=ko_s, v_out=vo_s)
     torch.cuda.synchronize()
@@ -251,7 +253,7 @@ def test_h2o_step(seed):
     ds = {"K": to_dev(st["K"], dtype), "V": to_dev(st["V"], dtype),
           "acc": torch.from_numpy(st["acc"].copy()).cuda(),
           "pos": torch.from_numpy(st["pos"].copy()).cuda()}
-    probs = torch.zeros((B, G * Hkv, C + 1), dtype=torch.float32, device="cuda")
+    probs = torch.full((B, G * Hkv, C + 1), float("nan"), device="cuda")
     out = torch.full((B, G * Hkv, d), float("nan"), dtype=torch.float32, device="cuda")
     ev_g = hk.h2o_step(to_dev(st["q"], dtype), to_dev(st["k_new"], dtype),
                        to_dev(st["v_new"], dtype), ds["K"], ds["V"], ds["acc"], ds["pos"], t,

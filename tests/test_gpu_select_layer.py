@@ -109,7 +109,7 @@ def test_repeated_calls_on_one_workspace():
     L, Hkv = 2, 5
     z = S.random_scores(seqlens, L, Hkv, seed=9)
     nb = hk.lib().hubkv_select_layer_workspace(2, hk._arr64(seqlens), L, Hkv)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws = torch.full((nb,), 255, dtype=torch.uint8, device="cuda")
     lo, hi = _bounds(seqlens, Hkv, 4, 16, 8)
     for frac in (0.1, 0.7, 0.1, 0.3):
         lk = [[int(a + frac * (b - a)) for a, b in zip(lo, hi)]] * L

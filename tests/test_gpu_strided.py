@@ -130,8 +130,10 @@ def test_compact_views_bitexact(dtype, d):
     vc = torch.full((L, Hkv, cap, d), -3.0, dtype=Kd.dtype, device=Kd.device)
     k1, v1 = hk.hubkv_compact(_token_major(Kd), kv[:, 1], idx, seqlens, kept,
                               k_out=kc[:, :, :Kt], v_out=vc[:, :, :Kt])
-    k2 = torch.empty((L, Kt, Hkv, d), dtype=Kd.dtype, device=Kd.device).permute(0, 2, 1, 3)
-    v2 = torch.empty((L, Kt, Hkv, d), dtype=Kd.dtype, device=Kd.device).permute(0, 2, 1, 3)
+    k2 = torch.full((L, Kt, Hkv, d), float("nan"), dtype=Kd.dtype,
+                    device=Kd.device).permute(0, 2, 1, 3)
+    v2 = torch.full((L, Kt, Hkv, d), float("nan"), dtype=Kd.dtype,
+                    device=Kd.device).permute(0, 2, 1, 3)
     hk.hubkv_compact(kv[:, 0], _padded(Vd, 11, 8), idx, seqlens, kept, k_out=k2, v_out=v2)
     torch.cuda.synchronize()
     assert torch.equal(k1, k0) and torch.equal(v1, v0)

@@ -1,10 +1,13 @@
 """token_scoring_top_amd -- MI355X (gfx950) KV-cache retention scoring and Top-K.
 
 Thin Python binding of libhubkv.so (include/hubkv.h).  It only marshals
-arguments: torch tensors become device pointers, the current torch stream
-becomes the HIP stream, and outputs/workspaces are allocated with torch.
-Every step of the path runs in the library's HIP kernels; there is no
-fallback, and importing the binding without the built library raises.
+arguments: torch tensors become device pointers, the given torch stream (the
+current one by default) becomes the HIP stream, and outputs/workspaces the
+caller does not pass are allocated with torch on that same stream, so the
+caching allocator never hands their blocks to other work while the kernels
+still use them.  Every step of the path runs in the library's HIP kernels;
+there is no fallback, and importing the binding without the built library
+raises.
 
 Functions (names follow the C ABI):
     hubkv_score(q, k, seqlens, W, scale, causal=True) -> (s, head_stats)
@@ -22,6 +25,7 @@ Functions (names follow the C ABI):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 import re
@@ -157,9 +161,42 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _on(stream):
+    """Allocation context of a call: the launch stream when one is given (the
+    caching allocator then orders reuse of the blocks after that stream's
+    work), else the current stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
+_POISON = False
+
+
+def set_output_poison(on: bool) -> None:
+    """When on, every output and workspace the binding allocates is filled
+    before the call (NaN for floating point, -2^31 for integers, which no
+    integer output of the library can hold, 0xff bytes for workspaces), so an
+    element a kernel never writes cannot pass for a result.  Off by default; the GPU tests turn it on."""
+    global _POISON
+    _POISON = bool(on)
+
+
+def _new(shape, dtype, device):
+    """An output tensor on the current stream (poisoned when asked)."""
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if _POISON:
+        t.fill_(float("nan") if t.is_floating_point() else -(1 << 31))
+    return t
+
+
 def _workspace(nbytes: int, device):
     torch = _torch()
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if _POISON:
+        t.fill_(255)
+    return t
 
 
 # -------------------------------------------------------------------------
@@ -177,24 +214,26 @@ def hubkv_score(q, k, seqlens: Sequence[int], W: int, scale: float, causal: bool
         raise ValueError("inconsistent q/k shapes")
     sl = _arr64(seqlens)
     dt = _dtype_code(q)
-    if s is None:
-        s = torch.empty((L, Hkv, T), dtype=torch.float32, device=q.device)
-    if head_stats is None:
-        head_stats = torch.empty((L, B, Hkv, 2), dtype=torch.float64, device=q.device)
-    nb = lib().hubkv_score_workspace(B, sl, L, Hq, Hkv, W, d, dt)
-    if workspace is None:
-        workspace = _workspace(nb, q.device)
-    if q.is_contiguous() and k.is_contiguous():
-        _check("hubkv_score", lib().hubkv_score(_ptr(q), _ptr(k), dt, B, sl, L, Hq, Hkv, W, d,
-                                                float(scale), int(bool(causal)), _ptr(s),
-                                                _ptr(head_stats), _ptr(workspace),
-                                                workspace.numel(), _stream(stream)))
-    else:
-        _check("hubkv_score_strided",
-               lib().hubkv_score_strided(_ptr(q, True), _strides3(q), _ptr(k, True),
-                                         _strides3(k), dt, B, sl, L, Hq, Hkv, W, d, float(scale),
-                                         int(bool(causal)), _ptr(s), _ptr(head_stats),
-                                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    with _on(stream):
+        if s is None:
+            s = _new((L, Hkv, T), torch.float32, q.device)
+        if head_stats is None:
+            head_stats = _new((L, B, Hkv, 2), torch.float64, q.device)
+        nb = lib().hubkv_score_workspace(B, sl, L, Hq, Hkv, W, d, dt)
+        if workspace is None:
+            workspace = _workspace(nb, q.device)
+        if q.is_contiguous() and k.is_contiguous():
+            _check("hubkv_score", lib().hubkv_score(_ptr(q), _ptr(k), dt, B, sl, L, Hq, Hkv, W, d,
+                                                    float(scale), int(bool(causal)), _ptr(s),
+                                                    _ptr(head_stats), _ptr(workspace),
+                                                    workspace.numel(), _stream(stream)))
+        else:
+            _check("hubkv_score_strided",
+                   lib().hubkv_score_strided(_ptr(q, True), _strides3(q), _ptr(k, True),
+                                             _strides3(k), dt, B, sl, L, Hq, Hkv, W, d,
+                                             float(scale), int(bool(causal)), _ptr(s),
+                                             _ptr(head_stats), _ptr(workspace), workspace.numel(),
+                                             _stream(stream)))
     return s, head_stats
 
 
@@ -206,18 +245,19 @@ def hubkv_refine(s, seqlens: Sequence[int], head_stats=None, beta_in=None, pool:
     L, Hkv, T = s.shape
     B = len(seqlens)
     sl = _arr64(seqlens)
-    if z is None:
-        z = torch.empty_like(s)
-    if beta_out is None:
-        beta_out = torch.empty((L, B, Hkv), dtype=torch.float32, device=s.device)
-    nb = lib().hubkv_refine_workspace(B, sl, L, Hkv)
-    if workspace is None:
-        workspace = _workspace(nb, s.device)
-    _check("hubkv_refine", lib().hubkv_refine(_ptr(s), B, sl, L, Hkv, _ptr(head_stats),
-                                              _ptr(beta_in), int(pool), float(gamma),
-                                              float(beta_lo), float(beta_hi), float(r), _ptr(z),
-                                              _ptr(beta_out), _ptr(workspace), workspace.numel(),
-                                              _stream(stream)))
+    with _on(stream):
+        if z is None:
+            z = _new((L, Hkv, T), torch.float32, s.device)
+        if beta_out is None:
+            beta_out = _new((L, B, Hkv), torch.float32, s.device)
+        nb = lib().hubkv_refine_workspace(B, sl, L, Hkv)
+        if workspace is None:
+            workspace = _workspace(nb, s.device)
+        _check("hubkv_refine", lib().hubkv_refine(_ptr(s), B, sl, L, Hkv, _ptr(head_stats),
+                                                  _ptr(beta_in), int(pool), float(gamma),
+                                                  float(beta_lo), float(beta_hi), float(r),
+                                                  _ptr(z), _ptr(beta_out), _ptr(workspace),
+                                                  workspace.numel(), _stream(stream)))
     return z, beta_out
 
 
@@ -227,11 +267,12 @@ def hubkv_select(z, seqlens: Sequence[int], kept: Sequence[int], n_sink: int, n_
     torch = _torch()
     L, Hkv, T = z.shape
     B = len(seqlens)
-    if idx is None:
-        idx = torch.empty((L, Hkv, int(sum(kept))), dtype=torch.int32, device=z.device)
-    _check("hubkv_select", lib().hubkv_select(_ptr(z), B, _arr64(seqlens), L, Hkv, _arr64(kept),
-                                              int(n_sink), int(n_recent), _ptr(idx),
-                                              _stream(stream)))
+    with _on(stream):
+        if idx is None:
+            idx = _new((L, Hkv, int(sum(kept))), torch.int32, z.device)
+        _check("hubkv_select", lib().hubkv_select(_ptr(z), B, _arr64(seqlens), L, Hkv,
+                                                  _arr64(kept), int(n_sink), int(n_recent),
+                                                  _ptr(idx), _stream(stream)))
     return idx
 
 
@@ -239,29 +280,31 @@ def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], 
                   v_out=None, stream=None):
     """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [L][Hkv][sum kept][d] (any of
     the four may be a view with a contiguous last axis)."""
-    torch = _torch()
     L, Hkv, T, d = k_in.shape
     K = int(sum(kept))
-    if k_out is None:
-        k_out = torch.empty((L, Hkv, K, d), dtype=k_in.dtype, device=k_in.device)
-    if v_out is None:
-        v_out = torch.empty((L, Hkv, K, d), dtype=v_in.dtype, device=v_in.device)
-    for t, shape in ((v_in, (L, Hkv, T, d)), (k_out, (L, Hkv, K, d)), (v_out, (L, Hkv, K, d))):
-        if tuple(t.shape) != shape or t.dtype != k_in.dtype:
-            raise ValueError("inconsistent k/v shapes or dtypes")
-    dt = _dtype_code(k_in)
-    if all(t.is_contiguous() for t in (k_in, v_in, k_out, v_out)):
-        _check("hubkv_compact", lib().hubkv_compact(_ptr(k_in), _ptr(v_in), dt, _ptr(idx),
-                                                    len(seqlens), _arr64(seqlens), _arr64(kept),
-                                                    L, Hkv, d, _ptr(k_out), _ptr(v_out),
-                                                    _stream(stream)))
-    else:
-        _check("hubkv_compact_strided",
-               lib().hubkv_compact_strided(_ptr(k_in, True), _strides3(k_in), _ptr(v_in, True),
-                                           _strides3(v_in), dt, _ptr(idx), len(seqlens),
-                                           _arr64(seqlens), _arr64(kept), L, Hkv, d,
-                                           _ptr(k_out, True), _strides3(k_out),
-                                           _ptr(v_out, True), _strides3(v_out), _stream(stream)))
+    with _on(stream):
+        if k_out is None:
+            k_out = _new((L, Hkv, K, d), k_in.dtype, k_in.device)
+        if v_out is None:
+            v_out = _new((L, Hkv, K, d), v_in.dtype, v_in.device)
+        for t, shape in ((v_in, (L, Hkv, T, d)), (k_out, (L, Hkv, K, d)),
+                         (v_out, (L, Hkv, K, d))):
+            if tuple(t.shape) != shape or t.dtype != k_in.dtype:
+                raise ValueError("inconsistent k/v shapes or dtypes")
+        dt = _dtype_code(k_in)
+        if all(t.is_contiguous() for t in (k_in, v_in, k_out, v_out)):
+            _check("hubkv_compact", lib().hubkv_compact(_ptr(k_in), _ptr(v_in), dt, _ptr(idx),
+                                                        len(seqlens), _arr64(seqlens),
+                                                        _arr64(kept), L, Hkv, d, _ptr(k_out),
+                                                        _ptr(v_out), _stream(stream)))
+        else:
+            _check("hubkv_compact_strided",
+                   lib().hubkv_compact_strided(_ptr(k_in, True), _strides3(k_in),
+                                               _ptr(v_in, True), _strides3(v_in), dt, _ptr(idx),
+                                               len(seqlens), _arr64(seqlens), _arr64(kept), L,
+                                               Hkv, d, _ptr(k_out, True), _strides3(k_out),
+                                               _ptr(v_out, True), _strides3(v_out),
+                                               _stream(stream)))
     return k_out, v_out
 
 
@@ -274,20 +317,21 @@ def hubkv_nestedkv(k, seqlens: Sequence[int], nblocks: int = 32, window: int = 6
     L, Hkv, T, d = k.shape
     B = len(seqlens)
     sl = _arr64(seqlens)
-    if s is None:
-        s = torch.empty((L, Hkv, T), dtype=torch.float32, device=k.device)
-    if want_parts and anomalies is None:
-        anomalies = torch.empty((L, Hkv, T, 3), dtype=torch.float32, device=k.device)
-    if want_parts and weights is None:
-        weights = torch.empty((L, B, Hkv, 3), dtype=torch.float32, device=k.device)
-    nb = lib().hubkv_nestedkv_workspace(B, sl, L, Hkv, d, int(nblocks))
-    if workspace is None:
-        workspace = _workspace(nb, k.device)
-    lp = (C.c_float * 3)(*[float(x) for x in log_prior])
-    _check("hubkv_nestedkv", lib().hubkv_nestedkv(
-        _ptr(k), _dtype_code(k), B, sl, L, Hkv, d, int(nblocks), int(window),
-        C.cast(lp, C.c_void_p), float(theta), _ptr(s), _ptr(anomalies), _ptr(weights),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+    with _on(stream):
+        if s is None:
+            s = _new((L, Hkv, T), torch.float32, k.device)
+        if want_parts and anomalies is None:
+            anomalies = _new((L, Hkv, T, 3), torch.float32, k.device)
+        if want_parts and weights is None:
+            weights = _new((L, B, Hkv, 3), torch.float32, k.device)
+        nb = lib().hubkv_nestedkv_workspace(B, sl, L, Hkv, d, int(nblocks))
+        if workspace is None:
+            workspace = _workspace(nb, k.device)
+        lp = (C.c_float * 3)(*[float(x) for x in log_prior])
+        _check("hubkv_nestedkv", lib().hubkv_nestedkv(
+            _ptr(k), _dtype_code(k), B, sl, L, Hkv, d, int(nblocks), int(window),
+            C.cast(lp, C.c_void_p), float(theta), _ptr(s), _ptr(anomalies), _ptr(weights),
+            _ptr(workspace), workspace.numel(), _stream(stream)))
     return (s, anomalies, weights) if want_parts else s
 
 
@@ -303,34 +347,35 @@ def hubkv_select_layer(z, seqlens: Sequence[int], layer_kept, n_sink: int, n_rec
     lk = [int(x) for row in layer_kept for x in (row if hasattr(row, "__len__") else [row])]
     if len(lk) != L * B:
         raise ValueError(f"layer_kept must hold L * B = {L * B} totals")
-    if idx is None:
-        idx = torch.empty(sum(lk), dtype=torch.int32, device=z.device)
-    if head_kept is None:
-        head_kept = torch.empty((L, B, Hkv), dtype=torch.int32, device=z.device)
-    nb = lib().hubkv_select_layer_workspace(B, sl, L, Hkv)
-    if workspace is None:
-        workspace = _workspace(nb, z.device)
-    _check("hubkv_select_layer", lib().hubkv_select_layer(
-        _ptr(z), B, sl, L, Hkv, _arr64(lk), int(n_sink), int(n_recent), int(floor_min),
-        _ptr(idx), _ptr(head_kept), _ptr(workspace), workspace.numel(), _stream(stream)))
+    with _on(stream):
+        if idx is None:
+            idx = _new(sum(lk), torch.int32, z.device)
+        if head_kept is None:
+            head_kept = _new((L, B, Hkv), torch.int32, z.device)
+        nb = lib().hubkv_select_layer_workspace(B, sl, L, Hkv)
+        if workspace is None:
+            workspace = _workspace(nb, z.device)
+        _check("hubkv_select_layer", lib().hubkv_select_layer(
+            _ptr(z), B, sl, L, Hkv, _arr64(lk), int(n_sink), int(n_recent), int(floor_min),
+            _ptr(idx), _ptr(head_kept), _ptr(workspace), workspace.numel(), _stream(stream)))
     return idx, head_kept
 
 
 def hubkv_compact_layer(k_in, v_in, idx, head_kept, seqlens: Sequence[int], layer_kept,
                         k_out=None, v_out=None, stream=None):
     """k_in/v_in [L][Hkv][T][d] -> k_out/v_out [sum layer_kept][d] in idx's order."""
-    torch = _torch()
     L, Hkv, T, d = k_in.shape
     B = len(seqlens)
     lk = [int(x) for row in layer_kept for x in (row if hasattr(row, "__len__") else [row])]
     K = sum(lk)
-    if k_out is None:
-        k_out = torch.empty((K, d), dtype=k_in.dtype, device=k_in.device)
-    if v_out is None:
-        v_out = torch.empty((K, d), dtype=v_in.dtype, device=v_in.device)
-    _check("hubkv_compact_layer", lib().hubkv_compact_layer(
-        _ptr(k_in), _ptr(v_in), _dtype_code(k_in), _ptr(idx), _ptr(head_kept), B,
-        _arr64(seqlens), L, Hkv, _arr64(lk), d, _ptr(k_out), _ptr(v_out), _stream(stream)))
+    with _on(stream):
+        if k_out is None:
+            k_out = _new((K, d), k_in.dtype, k_in.device)
+        if v_out is None:
+            v_out = _new((K, d), v_in.dtype, v_in.device)
+        _check("hubkv_compact_layer", lib().hubkv_compact_layer(
+            _ptr(k_in), _ptr(v_in), _dtype_code(k_in), _ptr(idx), _ptr(head_kept), B,
+            _arr64(seqlens), L, Hkv, _arr64(lk), d, _ptr(k_out), _ptr(v_out), _stream(stream)))
     return k_out, v_out
 
 
@@ -347,17 +392,19 @@ def h2o_step(q, k_new, v_new, k_cache, v_cache, acc, pos, t, scale: float, n_sin
     B, Hq, d = q.shape
     _, Hkv, Cs, _ = k_cache.shape
     tt = [int(t)] * B if isinstance(t, int) else [int(x) for x in t]
-    if evicted is None:
-        evicted = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
     for name, x, shape in (("probs", probs, (B, Hq, Cs + 1)), ("out", out, (B, Hq, d))):
         if x is not None and (x.dtype != torch.float32 or tuple(x.shape) != shape):
             raise ValueError(f"{name} must be float32 of shape {shape}")
     name = "h2o_step_ring" if ring else "h2o_step"
-    _check(name, getattr(lib(), name)(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q),
-                                      _ptr(k_cache), _ptr(v_cache), _ptr(acc), _ptr(pos),
-                                      _arr64(tt), B, Hq, Hkv, d, Cs, int(n_sink), int(n_recent),
-                                      float(scale), int(bool(include_self)), _ptr(evicted),
-                                      _ptr(probs), _ptr(out), _stream(stream)))
+    with _on(stream):
+        if evicted is None:
+            evicted = _new((B, Hkv), torch.int32, q.device)
+        _check(name, getattr(lib(), name)(_ptr(q), _ptr(k_new), _ptr(v_new), _dtype_code(q),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(acc), _ptr(pos),
+                                          _arr64(tt), B, Hq, Hkv, d, Cs, int(n_sink),
+                                          int(n_recent), float(scale), int(bool(include_self)),
+                                          _ptr(evicted), _ptr(probs), _ptr(out),
+                                          _stream(stream)))
     return evicted
 
 

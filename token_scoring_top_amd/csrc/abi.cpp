@@ -26,6 +26,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;  // positions are int32
+// Longest sequence: kernels do their position arithmetic in int32, including
+// rounding a length up to a whole number of tiles or select rounds (at most
+// 2^20 positions), so every sequence stays below 2^30.
+constexpr int64_t kMaxSeqLen = (int64_t)1 << 30;
 
 // Validate the sequence table and fill it; tile size `tile` sets tile_off.
 int make_table(SeqTable& st, int B, const int64_t* seqlens, int tile) {
@@ -36,7 +40,7 @@ int make_table(SeqTable& st, int B, const int64_t* seqlens, int tile) {
   int64_t cu = 0, tiles = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t n = seqlens[b];
-    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    if (n < 1 || n >= kMaxSeqLen) return HUBKV_EINVAL;
     st.N[b] = n;
     st.cu[b] = cu;
     st.tile_off[b] = (int32_t)tiles;
@@ -130,7 +134,7 @@ int make_lsel(LselArgs& a, int B, const int64_t* seqlens, int L, int Hkv, const 
   int64_t cu = 0, ch = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t n = seqlens[b];
-    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    if (n < 1 || n >= kMaxSeqLen) return HUBKV_EINVAL;
     const int64_t P = hubkv_protected_count(n, n_sink, n_recent);
     a.N[b] = (int32_t)n;
     a.cu[b] = cu;
@@ -170,7 +174,7 @@ int make_nkv(NkvArgs& a, int B, const int64_t* seqlens, int L, int Hkv, int d, i
   int64_t cu = 0, tiles = 0, blks = 0, ats = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t n = seqlens[b];
-    if (n < 1 || n >= kMaxTokens) return HUBKV_EINVAL;
+    if (n < 1 || n >= kMaxSeqLen) return HUBKV_EINVAL;
     a.at_off[b] = (int32_t)ats;
     ats += (n + kNkvAnTile - 1) / kNkvAnTile;
     const int64_t bs = (n + nblocks - 1) / nblocks;
@@ -320,7 +324,7 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
   if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
   int64_t T = 0;
   for (int b = 0; b < B; ++b) {
-    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens) return HUBKV_EINVAL;
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxSeqLen) return HUBKV_EINVAL;
     T += seqlens[b];
   }
   // Bounds that check_score_shape implies, so the packed strides cannot overflow.
@@ -429,7 +433,7 @@ int hubkv_compact(const void* k_in, const void* v_in, int dtype, const int32_t* 
   if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
   int64_t T = 0, K = 0;
   for (int b = 0; b < B; ++b) {
-    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens || kept[b] < 0 || kept[b] > seqlens[b])
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxSeqLen || kept[b] < 0 || kept[b] > seqlens[b])
       return HUBKV_EINVAL;
     T += seqlens[b];
     K += kept[b];
@@ -450,7 +454,7 @@ size_t hubkv_select_layer_workspace(int B, const int64_t* seqlens, int L, int Hk
   a.Hkv = Hkv;
   int64_t ch = 0;
   for (int b = 0; b < B; ++b) {
-    if (seqlens[b] < 1 || seqlens[b] >= kMaxTokens) return 0;
+    if (seqlens[b] < 1 || seqlens[b] >= kMaxSeqLen) return 0;
     ch += (seqlens[b] + kLselChunk - 1) / kLselChunk;
   }
   if (ch > 65535) return 0;
