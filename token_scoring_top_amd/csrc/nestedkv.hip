@@ -20,12 +20,12 @@
 //      a block (16-byte pieces, a row over LPR lanes, several rows per wave
 //      instruction);
 //   2  block sums and their norms (tiles added in a fixed order);
-//   3  anomalies over tiles of kNkvAnTile keys: the sequence sum from the
-//      block sums, in order; walkers (the lanes of one row slot) each carry
-//      the window sum S along a contiguous run of rows (S += k^_new - k^_old,
-//      the old row reloaded from cache and renormalised with its stored
-//      inverse norm), so the stable, episodic and current cosines are dot
-//      products folded over a row's lanes; per-tile extremes of each anomaly;
+//   3  anomalies over tiles of kNkvAnTile keys, one key row per lane: the
+//      sequence sum from the block sums, in order; the current-window sum of
+//      each row is a cross-lane prefix (DPP scans) of the normalised keys of
+//      its 64-row segment plus the suffix of the previous segment, so the
+//      stable, episodic and current cosines are lane-local dot products;
+//      per-tile extremes of each anomaly;
 //   4  per-head weights from the tiles' extremes, routing, the score.
 // Cosines are scale-free, so sums stand in for means.
 #include "internal.hpp"
