@@ -78,6 +78,7 @@ extern "C" {
 #define HUBKV_EALIGN (-3)     /* a pointer is null or not aligned as required    */
 #define HUBKV_EWORKSPACE (-4) /* workspace missing or smaller than required      */
 #define HUBKV_EHIP (-5)       /* a HIP launch failed; see hubkv_last_hip_error() */
+#define HUBKV_ESCRATCH (-6)   /* the problem needs more than the fixed scratch   */
 
 /* Element types of Q, K and V. */
 #define HUBKV_F32 0
@@ -108,6 +109,30 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
                 int L, int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
                 double* head_stats /* nullable */, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * hubkv_score_noalloc -- hubkv_score for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, computation and
+ * results (bit for bit) as hubkv_score without the workspace: its scratch is
+ * a fixed array of HUBKV_SCORE_NOALLOC_BYTES that the library holds on every
+ * device it runs on, until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks the array's device address up once.  A problem whose
+ * hubkv_score_workspace() exceeds that size returns HUBKV_ESCRATCH on the
+ * host, before anything is enqueued.  Every call on a device shares that
+ * device's array and needs no clearing of it (each call writes every byte it
+ * reads), so calls that overlap in time on one device (on different streams,
+ * or from several host threads) race on it and must be serialised by the
+ * caller.  The device is the one `stream` belongs to (the current device for
+ * the null stream).
+ */
+#define HUBKV_SCORE_NOALLOC_BYTES (16u << 20)
+
+int hubkv_score_noalloc(const void* q, const void* k, int dtype, int B,
+                        const int64_t* seqlens /* host */, int L, int Hq, int Hkv, int W, int d,
+                        float scale, int causal, float* s, double* head_stats /* nullable */,
+                        void* stream);
 
 /*
  * hubkv_score_strided -- hubkv_score on strided Q and K views (same

@@ -308,3 +308,25 @@ def test_sequence_length_limit():
     # one below the limit passes the length check
     sl = a64([(1 << 30) - 1])
     assert L.hubkv_refine_workspace(1, sl, 1, 1) > 0
+
+
+def test_score_noalloc_rejects_problems_beyond_its_scratch():
+    """hubkv_score_noalloc refuses, on the host, a problem whose workspace
+    exceeds the library's fixed scratch (HUBKV_SCORE_NOALLOC_BYTES = 16 MiB)."""
+    L = hk.lib()
+    ESCRATCH = -6
+    assert L.hubkv_strerror(ESCRATCH)
+    # 64 layers x 64 KV heads x 512 query rows: the workspace holds (m, l) per
+    # row for every (layer, head, chunk)
+    sl = a64([2048])
+    nb = L.hubkv_score_workspace(1, sl, 64, 512, 64, 64, 128, 1)
+    assert nb > (16 << 20)
+    assert L.hubkv_score_noalloc(P, P, 1, 1, sl, 64, 512, 64, 64, 128, 0.1, 1, P, None,
+                                 None) == ESCRATCH
+    # invalid arguments are still rejected first, as hubkv_score rejects them
+    assert L.hubkv_score_noalloc(P, P, 1, 1, a64([512]), 1, 4, 4, 32, 96, 0.1, 1, P, None,
+                                 None) == EDTYPE
+    assert L.hubkv_score_noalloc(P, P, 1, 1, a64([10]), 1, 4, 4, 32, 64, 0.1, 1, P, None,
+                                 None) == EINVAL
+    assert L.hubkv_score_noalloc(P + 2, P, 1, 1, a64([512]), 1, 4, 4, 32, 64, 0.1, 1, P, None,
+                                 None) == EALIGN

@@ -11,6 +11,7 @@ raises.
 
 Functions (names follow the C ABI):
     hubkv_score(q, k, seqlens, W, scale, causal=True) -> (s, head_stats)
+    hubkv_score_noalloc(q, k, seqlens, W, scale, ...)  -> (s, head_stats), no workspace
     hubkv_refine(s, seqlens, ...)                      -> (z, beta)
     hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
     hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
@@ -37,7 +38,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "hubkv.h")
 
 HUBKV_F32, HUBKV_BF16 = 0, 1
 STATUS = {0: "HUBKV_OK", -1: "HUBKV_EINVAL", -2: "HUBKV_EDTYPE", -3: "HUBKV_EALIGN",
-          -4: "HUBKV_EWORKSPACE", -5: "HUBKV_EHIP"}
+          -4: "HUBKV_EWORKSPACE", -5: "HUBKV_EHIP", -6: "HUBKV_ESCRATCH"}
 
 
 class HubkvError(RuntimeError):
@@ -62,6 +63,8 @@ _SIGS = {
                           _vp]),
     "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp]),
     "hubkv_compact": (_i, [_vp, _vp, _i, _vp, _i, _i64p, _i64p, _i, _i, _i, _vp, _vp, _vp]),
+    "hubkv_score_noalloc": (_i, [_vp, _vp, _i, _i, _i64p, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                 _vp]),
     "hubkv_score_strided": (_i, [_vp, _i64p, _vp, _i64p, _i, _i, _i64p, _i, _i, _i, _i, _i, _f,
                                  _i, _vp, _vp, _vp, _sz, _vp]),
     "hubkv_compact_strided": (_i, [_vp, _i64p, _vp, _i64p, _i, _vp, _i, _i64p, _i64p, _i, _i,
@@ -234,6 +237,29 @@ def hubkv_score(q, k, seqlens: Sequence[int], W: int, scale: float, causal: bool
                                              float(scale), int(bool(causal)), _ptr(s),
                                              _ptr(head_stats), _ptr(workspace), workspace.numel(),
                                              _stream(stream)))
+    return s, head_stats
+
+
+def hubkv_score_noalloc(q, k, seqlens: Sequence[int], W: int, scale: float, causal: bool = True,
+                        s=None, head_stats=None, stream=None):
+    """hubkv_score on the library's fixed per-device scratch (no workspace,
+    no allocation inside the library); q and k packed.  Outputs the caller
+    does not pass are allocated here, by torch."""
+    torch = _torch()
+    L, Hq, BW, d = q.shape
+    L2, Hkv, T, d2 = k.shape
+    B = len(seqlens)
+    if L2 != L or d2 != d or BW != B * W or T != sum(seqlens) or q.dtype != k.dtype:
+        raise ValueError("inconsistent q/k shapes")
+    with _on(stream):
+        if s is None:
+            s = _new((L, Hkv, T), torch.float32, q.device)
+        if head_stats is None:
+            head_stats = _new((L, B, Hkv, 2), torch.float64, q.device)
+        _check("hubkv_score_noalloc",
+               lib().hubkv_score_noalloc(_ptr(q), _ptr(k), _dtype_code(q), B, _arr64(seqlens), L,
+                                         Hq, Hkv, W, d, float(scale), int(bool(causal)), _ptr(s),
+                                         _ptr(head_stats), _stream(stream)))
     return s, head_stats
 
 

@@ -31,6 +31,9 @@ constexpr int64_t kMaxTokens = (int64_t)1 << 31;  // positions are int32
 // 2^20 positions), so every sequence stays below 2^30.
 constexpr int64_t kMaxSeqLen = (int64_t)1 << 30;
 
+static_assert(kScoreScratchBytes == (size_t)HUBKV_SCORE_NOALLOC_BYTES,
+              "the header states the fixed score scratch size");
+
 // Validate the sequence table and fill it; tile size `tile` sets tile_off.
 int make_table(SeqTable& st, int B, const int64_t* seqlens, int tile) {
   if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
@@ -246,6 +249,43 @@ int h2o_impl(const void* q, const void* k_new, const void* v_new, int dtype, voi
                                     probs, out, (hipStream_t)stream));
 }
 
+// Validation and launch of the score, on a caller's workspace or (noalloc)
+// on the library's fixed per-device scratch.
+int score_impl(const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+               int dtype, int B, const int64_t* seqlens, int L, int Hq, int Hkv, int W, int d,
+               float scale, int causal, float* s, double* head_stats, void* workspace,
+               size_t workspace_bytes, void* stream, bool noalloc) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  SeqTable st;
+  if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
+  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, Hkv > 0 ? (Hq / Hkv) * W : 0, dtype);
+  if ((rc = make_table(st, B, seqlens, chunk))) return rc;
+  if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
+  if (!isfinite(scale)) return HUBKV_EINVAL;
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) T += st.N[b];
+  const int esize = dtype == HUBKV_BF16 ? 2 : 4;
+  const int64_t qext[3] = {L, Hq, (int64_t)B * W}, kext[3] = {L, Hkv, T};
+  if ((rc = check_strides(q_strides, qext, esize, d, false))) return rc;
+  if ((rc = check_strides(k_strides, kext, esize, d, false))) return rc;
+  if (!q || !k || !s || !aligned(q, 16) || !aligned(k, 16) || !aligned(s, 4)) return HUBKV_EALIGN;
+  if (head_stats && !aligned(head_stats, 8)) return HUBKV_EALIGN;
+  const ScoreGeom geo = score_geometry(st, L, Hq, Hkv, W, d, dtype);
+  char* ws = (char*)workspace;
+  if (noalloc) {
+    if (geo.bytes > kScoreScratchBytes) return HUBKV_ESCRATCH;
+    if ((rc = hip_status(score_scratch((hipStream_t)stream, &ws)))) return rc;
+  } else {
+    if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
+    if (!aligned(workspace, 256)) return HUBKV_EALIGN;
+  }
+  const ScoreStrides sd{q_strides[0], q_strides[1], q_strides[2],
+                        k_strides[0], k_strides[1], k_strides[2]};
+  return hip_status(launch_score(q, k, dtype, st, L, Hq, Hkv, W, d, sd, scale, causal, s,
+                                 head_stats, ws, geo, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -267,6 +307,7 @@ const char* hubkv_strerror(int status) {
     case HUBKV_EALIGN: return "null or misaligned pointer";
     case HUBKV_EWORKSPACE: return "workspace missing or too small";
     case HUBKV_EHIP: return "HIP launch failure";
+    case HUBKV_ESCRATCH: return "problem needs more scratch than the library's fixed array holds";
     default: return "unknown status";
   }
 }
@@ -291,36 +332,14 @@ int hubkv_score_strided(const void* q, const int64_t* q_strides, const void* k,
                         int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
                         double* head_stats, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  int rc = check_dtype_d(dtype, d);
-  if (rc) return rc;
-  SeqTable st;
-  if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
-  const int chunk = score_chunk(B, seqlens, (int64_t)L * Hkv, Hkv > 0 ? (Hq / Hkv) * W : 0, dtype);
-  if ((rc = make_table(st, B, seqlens, chunk))) return rc;
-  if ((rc = check_score_shape(L, Hq, Hkv, W, st))) return rc;
-  if (!isfinite(scale)) return HUBKV_EINVAL;
-  int64_t T = 0;
-  for (int b = 0; b < B; ++b) T += st.N[b];
-  const int esize = dtype == HUBKV_BF16 ? 2 : 4;
-  const int64_t qext[3] = {L, Hq, (int64_t)B * W}, kext[3] = {L, Hkv, T};
-  if ((rc = check_strides(q_strides, qext, esize, d, false))) return rc;
-  if ((rc = check_strides(k_strides, kext, esize, d, false))) return rc;
-  if (!q || !k || !s || !aligned(q, 16) || !aligned(k, 16) || !aligned(s, 4)) return HUBKV_EALIGN;
-  if (head_stats && !aligned(head_stats, 8)) return HUBKV_EALIGN;
-  const ScoreGeom geo = score_geometry(st, L, Hq, Hkv, W, d, dtype);
-  if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
-  if (!aligned(workspace, 256)) return HUBKV_EALIGN;
-  const ScoreStrides sd{q_strides[0], q_strides[1], q_strides[2],
-                        k_strides[0], k_strides[1], k_strides[2]};
-  return hip_status(launch_score(q, k, dtype, st, L, Hq, Hkv, W, d, sd, scale, causal, s,
-                                 head_stats, (char*)workspace, geo, (hipStream_t)stream));
+  return score_impl(q, q_strides, k, k_strides, dtype, B, seqlens, L, Hq, Hkv, W, d, scale, causal,
+                    s, head_stats, workspace, workspace_bytes, stream, false);
 }
 
-int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens, int L,
-                int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
-                double* head_stats, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = check_dtype_d(dtype, d);
-  if (rc) return rc;
+// Packed strides of Q [L][Hq][B*W][d] and K [L][Hkv][T][d]; validates what
+// they are computed from so they cannot overflow.
+static int packed_score_strides(int B, const int64_t* seqlens, int L, int Hq, int Hkv, int W,
+                                int d, int64_t qs[3], int64_t ks[3]) {
   if (B < 1 || B > kMaxSeqs || !seqlens) return HUBKV_EINVAL;
   int64_t T = 0;
   for (int b = 0; b < B; ++b) {
@@ -330,10 +349,35 @@ int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* s
   // Bounds that check_score_shape implies, so the packed strides cannot overflow.
   if (L < 1 || Hq < 1 || Hkv < 1 || W < 1 || W > 512 || Hkv > kMaxGridY || Hq > 512 * kMaxGridY)
     return HUBKV_EINVAL;
-  const int64_t qs[3] = {(int64_t)Hq * B * W * d, (int64_t)B * W * d, d};
-  const int64_t ks[3] = {(int64_t)Hkv * T * d, T * d, d};
-  return hubkv_score_strided(q, qs, k, ks, dtype, B, seqlens, L, Hq, Hkv, W, d, scale, causal, s,
-                             head_stats, workspace, workspace_bytes, stream);
+  qs[0] = (int64_t)Hq * B * W * d;
+  qs[1] = (int64_t)B * W * d;
+  qs[2] = d;
+  ks[0] = (int64_t)Hkv * T * d;
+  ks[1] = T * d;
+  ks[2] = d;
+  return HUBKV_OK;
+}
+
+int hubkv_score(const void* q, const void* k, int dtype, int B, const int64_t* seqlens, int L,
+                int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                double* head_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  int64_t qs[3], ks[3];
+  if ((rc = packed_score_strides(B, seqlens, L, Hq, Hkv, W, d, qs, ks))) return rc;
+  return score_impl(q, qs, k, ks, dtype, B, seqlens, L, Hq, Hkv, W, d, scale, causal, s,
+                    head_stats, workspace, workspace_bytes, stream, false);
+}
+
+int hubkv_score_noalloc(const void* q, const void* k, int dtype, int B, const int64_t* seqlens,
+                        int L, int Hq, int Hkv, int W, int d, float scale, int causal, float* s,
+                        double* head_stats, void* stream) {
+  int rc = check_dtype_d(dtype, d);
+  if (rc) return rc;
+  int64_t qs[3], ks[3];
+  if ((rc = packed_score_strides(B, seqlens, L, Hq, Hkv, W, d, qs, ks))) return rc;
+  return score_impl(q, qs, k, ks, dtype, B, seqlens, L, Hq, Hkv, W, d, scale, causal, s,
+                    head_stats, nullptr, 0, stream, true);
 }
 
 size_t hubkv_refine_workspace(int B, const int64_t* seqlens, int L, int Hkv) {

@@ -67,6 +67,14 @@ struct ScoreStrides {
   int64_t q_l, q_h, q_r, k_l, k_h, k_t;
 };
 
+// Score scratch the library holds itself, for callers that cannot allocate:
+// one fixed array per device (a file-scope __device__ array in score.hip).
+constexpr size_t kScoreScratchBytes = (size_t)16 << 20;
+
+// Device address of that array on the device `stream` runs on (the current
+// device for the null stream), looked up once per device.
+hipError_t score_scratch(hipStream_t stream, char** ptr);
+
 hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable& st, int L, int Hq,
                         int Hkv, int W, int d, const ScoreStrides& sd, float scale, int causal,
                         float* s, double* head_stats, char* ws, const ScoreGeom& geo,

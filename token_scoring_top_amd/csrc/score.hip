@@ -22,6 +22,8 @@
 // puts keys on the MFMA rows (row statistics become lane-local), pass 2 puts
 // queries on the rows (column sums become lane-local).  fp32 inputs use a
 // plain VALU path.
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace hubkv {
@@ -1016,6 +1018,53 @@ hipError_t launch_score(const void* q, const void* k, int dtype, const SeqTable&
   hipLaunchKernelGGL(stats_final, dim3((units + 63) / 64), dim3(64), 0, stream, st, L, Hkv,
                      geo.nchunk, (const double2*)part2, head_stats);
   return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// Fixed scratch for the allocation-free score entry point.  Each device that
+// runs the library holds its own copy of `scratch` until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol): the device address comes from hipGetSymbolAddress,
+// once per device with that device current, and is kept here.
+// --------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) char scratch[kScoreScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t score_scratch(hipStream_t stream, char** ptr) {
+  *ptr = nullptr;
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace hubkv
