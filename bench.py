@@ -129,102 +129,219 @@ def h2o_step_bytes(w, elem, with_out=False):
     return n
 
 
+# (sequence, KV head) units of the decode workload that the oracle follows
+# beside the GPU: one per sequence, KV heads spread over the 32
+DECODE_SAMPLE_UNITS = tuple((i, (5 * i + 3) % 32) for i in range(16))
+
+
+class DecodeStream:
+    """The decode workload streamed through h2o_step (or h2o_step_ring) on the
+    GPU for every (sequence, KV head) unit, with the oracle beside it on the
+    sampled units, each side running freely on its own state.  Both sides get
+    the same per-step inputs for those units: their rows of q, k and v come
+    from each unit's own seeded stream (synthetic.decode_unit_stream); every
+    other unit's rows are seeded normal draws made on the GPU.  The GPU records
+    each sampled unit's evicted position at every step; the oracle catches up
+    on demand and reports its candidates' margin, so a divergence can be
+    traced to a near-tie."""
+
+    def __init__(self, w, total, units=DECODE_SAMPLE_UNITS, ring=False, attn_out=False,
+                 with_oracle=True, block=256):
+        import numpy as np
+        import torch
+
+        import synthetic as S
+        self.np, self.torch = np, torch
+        self.w, self.total, self.ring, self.block = w, int(total), ring, block
+        self.units = [(b, g) for b, g in units if b < w.B and g < w.Hkv]
+        B, Hq, Hkv, d, C = w.B, w.Hq, w.Hkv, w.d, w.C
+        self.G = Hq // Hkv
+        dev = "cuda"
+        self.dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.Kc = torch.zeros((B, Hkv, C, d), dtype=self.dt, device=dev)
+        self.Vc = torch.zeros_like(self.Kc)
+        self.acc = torch.zeros((B, Hkv, C), dtype=torch.float32, device=dev)
+        self.pos = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if attn_out else None
+        self.gen = torch.Generator(device=dev)
+        self.gen.manual_seed(1000 * w.wid)
+        streams = [S.decode_unit_stream(w, b, g, self.total) for b, g in self.units]
+        self.uq = np.stack([x[0] for x in streams], 1)   # [total][units][G][d]
+        self.uk = np.stack([x[1] for x in streams], 1)   # [total][units][d]
+        self.uv = np.stack([x[2] for x in streams], 1)
+        nu = len(self.units)
+        self.ub = torch.tensor([b for b, _ in self.units], device=dev, dtype=torch.long)
+        self.ug = torch.tensor([g for _, g in self.units], device=dev, dtype=torch.long)
+        self.ev_gpu = np.full((self.total, nu), -2, np.int32)
+        self.t = 0
+        self.with_oracle = with_oracle
+        if with_oracle:
+            import oracle
+            self.oracle = oracle
+            self.ost = oracle.empty_state(nu, 1, C, d)
+            self.ev_orc = np.full((self.total, nu), -2, np.int32)
+            self.mg_orc = np.full((self.total, nu), np.inf, np.float32)
+            self.to = 0
+
+    def inputs(self, t0, n):
+        """q, k, v of steps [t0, t0 + n) on the device, [n][B][...][d]."""
+        torch, w = self.torch, self.w
+        B, Hq, Hkv, d, G = w.B, w.Hq, w.Hkv, w.d, self.G
+        q = torch.randn((n, B, Hq, d), generator=self.gen, device="cuda").to(self.dt)
+        k = torch.randn((n, B, Hkv, d), generator=self.gen, device="cuda").to(self.dt)
+        v = torch.randn((n, B, Hkv, d), generator=self.gen, device="cuda").to(self.dt)
+        uq = torch.from_numpy(self.uq[t0:t0 + n]).cuda().to(self.dt)
+        uk = torch.from_numpy(self.uk[t0:t0 + n]).cuda().to(self.dt)
+        uv = torch.from_numpy(self.uv[t0:t0 + n]).cuda().to(self.dt)
+        for i, (b, g) in enumerate(self.units):
+            q[:, b, g * G:(g + 1) * G] = uq[:, i]
+            k[:, b, g] = uk[:, i]
+            v[:, b, g] = uv[:, i]
+        return q, k, v
+
+    def launch(self, q, k, v, t, evicted, stream=None):
+        import token_scoring_top_amd as hk
+        w = self.w
+        hk.h2o_step(q, k, v, self.Kc, self.Vc, self.acc, self.pos, t, w.scale, w.n_sink,
+                    w.recent, bool(w.include_self), evicted=evicted, out=self.out,
+                    stream=stream, ring=self.ring)
+
+    def run_gpu(self, n, stream=None, oracle_beside=False):
+        """n more steps on the GPU (blocks of inputs drawn on the device); the
+        oracle follows block by block when asked."""
+        torch = self.torch
+        end = self.t + n
+        while self.t < end:
+            m = min(self.block, end - self.t)
+            q, k, v = self.inputs(self.t, m)
+            evs = torch.empty((m, self.w.B, self.w.Hkv), dtype=torch.int32, device="cuda")
+            for i in range(m):
+                self.launch(q[i], k[i], v[i], self.t + i, evs[i], stream)
+            if oracle_beside and self.with_oracle:
+                self.run_oracle(self.t)   # the previous blocks, while this one runs
+            self.record(self.t, evs[:, self.ub, self.ug])
+            self.t += m
+
+    def record(self, t0, ev_units):
+        ev = ev_units.cpu().numpy()
+        self.ev_gpu[t0:t0 + ev.shape[0]] = ev
+
+    def run_oracle(self, until):
+        w = self.w
+        while self.to < min(until, self.total):
+            t = self.to
+            ev, mg = self.oracle.h2o_step(self.ost, self.uq[t], self.uk[t][:, None],
+                                          self.uv[t][:, None], t, w.scale, w.n_sink, w.recent,
+                                          w.include_self, want_margin=True)
+            self.ev_orc[t] = ev[:, 0]
+            self.mg_orc[t] = mg[:, 0]
+            self.to += 1
+
+    def stats(self):
+        """Free-running agreement over the steps both sides have run."""
+        np = self.np
+        T = min(self.t, self.to)
+        evg, evo, mg = self.ev_gpu[:T], self.ev_orc[:T], self.mg_orc[:T]
+        evicting = (evg >= 0) | (evo >= 0)
+        same = evg == evo
+        prompt = self.w.prompt
+        dec = np.zeros_like(same)
+        dec[prompt:] = True
+        first, first_margin = [], []
+        for u in range(len(self.units)):
+            bad = np.flatnonzero(~same[:, u])
+            if bad.size:
+                first.append(int(bad[0]))
+                first_margin.append(float(mg[bad[0], u]))
+        # retained sets after step T (the GPU cache must be at the same step)
+        pos_g = self.pos[self.ub, self.ug].cpu().numpy()
+        overlap = [np.intersect1d(pos_g[u][pos_g[u] >= 0], self.ost["pos"][u, 0][
+            self.ost["pos"][u, 0] >= 0]).size / self.w.C for u in range(len(self.units))]
+        return {
+            "steps": int(T), "units": [list(x) for x in self.units],
+            "evictions_compared": int(evicting.sum()),
+            "identical_eviction_frac": float(same[evicting].mean()) if evicting.any() else 1.0,
+            "identical_eviction_frac_decode": (float(same[evicting & dec].mean())
+                                               if (evicting & dec).any() else None),
+            "units_diverged": len(first),
+            "first_divergence_steps": first,
+            "first_divergence_oracle_margins": first_margin,
+            "final_set_overlap_mean": float(np.mean(overlap)),
+            "final_set_overlap_min": float(np.min(overlap)),
+        }
+
+
 def bench_decode(args, w):
     """Streaming H2O decode: the prompt is streamed through h2o_step to build
-    the cache state (untimed), then `steps` decode steps are timed."""
+    the cache state (untimed), then `steps` decode steps are timed.  With the
+    CPU baseline on, the oracle also follows sampled units beside the GPU
+    through the whole stream (free running) and the line reports how often
+    both evict the same token and how far their final caches overlap."""
     import numpy as np
     import torch
 
-    import token_scoring_top_amd as hk
-
     steps = 512 if args.steps is None else args.steps
     B, Hq, Hkv, d, C = w.B, w.Hq, w.Hkv, w.d, w.C
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     elem = 2 if w.dtype == "bf16" else 4
-    dev = "cuda"
-    Kc = torch.zeros((B, Hkv, C, d), dtype=dt, device=dev)
-    Vc = torch.zeros_like(Kc)
-    acc = torch.zeros((B, Hkv, C), dtype=torch.float32, device=dev)
-    pos = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
-    ev = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-    o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if args.attn_out else None
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(1000 * w.wid)
+    follow = not args.no_cpu_baseline
+    total = w.prompt + args.warmup + 2 * steps
+    ds = DecodeStream(w, total, ring=args.ring, attn_out=args.attn_out, with_oracle=follow)
     stream = torch.cuda.current_stream()
-    blk = 256
-
-    def inputs(n):
-        # synthetic per-step q, k, v ~ N(0, 1), rounded to the element type
-        q = torch.randn((n, B, Hq, d), generator=gen, device=dev).to(dt)
-        k = torch.randn((n, B, Hkv, d), generator=gen, device=dev).to(dt)
-        v = torch.randn((n, B, Hkv, d), generator=gen, device=dev).to(dt)
-        return q, k, v
-
-    def run(t0, n, evs=None):
-        t = t0
-        while t < t0 + n:
-            m = min(blk, t0 + n - t)
-            q, k, v = inputs(m)
-            for i in range(m):
-                if evs is not None:
-                    evs[t - t0][0].record(stream)
-                hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t, w.scale, w.n_sink, w.recent,
-                            bool(w.include_self), evicted=ev, out=o, stream=stream,
-                            ring=args.ring)
-                if evs is not None:
-                    evs[t - t0][1].record(stream)
-                t += 1
-        return t
-
-    # the prompt, streamed token by token (builds the retained cache)
-    t = run(0, w.prompt)
-    t = run(t, args.warmup)
+    # the prompt and the warm-up steps, streamed token by token (builds the
+    # retained cache); the oracle follows block by block on the host
+    ds.run_gpu(w.prompt + args.warmup, stream, oracle_beside=follow)
+    t = ds.t
     # timed decode steps; inputs are drawn before the timed region
-    q, k, v = inputs(steps)
+    q, k, v = ds.inputs(t, steps)
+    evs = torch.empty((steps, B, Hkv), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, out=o, stream=stream, ring=args.ring)
+        ds.launch(q[i], k[i], v[i], t + i, evs[i], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    t += steps
+    ds.record(t, evs[:, ds.ub, ds.ug])
+    ds.t = t = t + steps
     ms_step = (t1 - t0) * 1e3 / steps
     # per-launch kernel time from HIP events on the launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    q, k, v = inputs(steps)
+    ev_t = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(steps)]
+    q, k, v = ds.inputs(t, steps)
     for i in range(steps):
-        evs[i][0].record(stream)
-        hk.h2o_step(q[i], k[i], v[i], Kc, Vc, acc, pos, t + i, w.scale, w.n_sink, w.recent,
-                    bool(w.include_self), evicted=ev, out=o, stream=stream, ring=args.ring)
-        evs[i][1].record(stream)
+        ev_t[i][0].record(stream)
+        ds.launch(q[i], k[i], v[i], t + i, evs[i], stream)
+        ev_t[i][1].record(stream)
     torch.cuda.synchronize()
-    t += steps
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    nbytes = h2o_step_bytes(w, elem, o is not None)
+    ds.record(t, evs[:, ds.ub, ds.ug])
+    ds.t = t = t + steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_t]))
+    nbytes = h2o_step_bytes(w, elem, args.attn_out)
     ach = nbytes / (k_ms / 1e3) / 1e9
     dec_traffic = None
-    if (o is None and not args.ring and DECODE_TRAFFIC["workload"] == w.wid
+    if (not args.attn_out and not args.ring and DECODE_TRAFFIC["workload"] == w.wid
             and DECODE_TRAFFIC["sha256"] == _source_sha(("h2o_step.hip", "internal.hpp"))):
         dec_traffic = DECODE_TRAFFIC["fetch_bytes"] + DECODE_TRAFFIC["write_bytes"]
 
     cpu = None
-    if not args.no_cpu_baseline:
+    free = None
+    if follow:
         import oracle
         nthreads = min(16, _cores())
         oracle.set_threads(nthreads)
         used = oracle.get_threads()
+        # the oracle's free-running units catch up with the GPU's last step
+        ds.run_oracle(ds.t)
+        free = ds.stats()
         # bounded sample: decode steps of the oracle from a copy of the GPU state
         def f32(x):
             return np.ascontiguousarray(x.float().cpu().numpy())
-        state = {"K": f32(Kc), "V": f32(Vc), "acc": acc.cpu().numpy().copy(),
-                 "pos": pos.cpu().numpy().copy()}
-        qs, ks, vs = (f32(x) for x in inputs(64))
+        state = {"K": f32(ds.Kc), "V": f32(ds.Vc), "acc": ds.acc.cpu().numpy().copy(),
+                 "pos": ds.pos.cpu().numpy().copy()}
+        qs, ks, vs = (f32(x) for x in ds.inputs(min(t, total - 64), 64))
         reps, tc0 = 0, time.perf_counter()
         while reps < 64:
             oracle.h2o_step(state, qs[reps], ks[reps], vs[reps], t + reps, w.scale, w.n_sink,
-                            w.recent, w.include_self, want_out=o is not None)
+                            w.recent, w.include_self, want_out=args.attn_out)
             reps += 1
             if time.perf_counter() - tc0 >= args.cpu_budget_s:
                 break
@@ -250,13 +367,14 @@ def bench_decode(args, w):
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "heavy": w.heavy,
                    "recent": w.recent, "prompt_steps_untimed": w.prompt,
-                   "attention_output": o is not None,
+                   "attention_output": bool(args.attn_out),
                    "slot_layout": "ring" if args.ring else "fixed",
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": dec_traffic, "op": "h2o_step",
                      "kernels": "h2o_step_kernel", "algorithmic_bytes": nbytes},
         "kernel_ms": k_ms,
+        "free_running": free,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

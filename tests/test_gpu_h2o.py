@@ -309,3 +309,46 @@ def test_attention_output_free_running_stream(dtype, include_self):
         assert np.all(mg[newly] <= 1e-4), f"step {t}: divergence without a near-tie"
         diverged |= newly
     assert diverged.mean() <= 0.5
+
+
+def test_free_running_decode_workload():
+    """The decode workload at full size (16 sequences x 32 KV heads, 2048 heavy
+    + 2048 recent slots, d 128, bf16) streamed through h2o_step from an empty
+    cache: the 16384-token prompt, then the 512 decode steps.  The oracle
+    follows 16 sampled (sequence, KV head) units beside the GPU, each side on
+    its own state, fed the same per-step inputs.  Every first divergence of a
+    unit must be a near-tie of the oracle's eviction candidates (their two
+    smallest accumulated scores within the bf16 bar); a unit that never
+    diverges must end with the same tokens in the same slots and the same
+    accumulated scores within that bar."""
+    import bench
+    w = S.workload(4)
+    total = w.prompt + w.decode
+    note(f"  streaming {total} steps on the GPU, the oracle beside it on "
+         f"{len(bench.DECODE_SAMPLE_UNITS)} units")
+    ds = bench.DecodeStream(w, total)
+    ds.run_gpu(total, oracle_beside=True)
+    ds.run_oracle(total)
+    st = ds.stats()
+    note(f"  identical evictions {st['identical_eviction_frac']:.5f} "
+         f"(decode steps {st['identical_eviction_frac_decode']:.5f}), "
+         f"{st['units_diverged']} unit(s) diverged at steps {st['first_divergence_steps']} "
+         f"with oracle margins {st['first_divergence_oracle_margins']}, "
+         f"final-set overlap mean {st['final_set_overlap_mean']:.5f} "
+         f"min {st['final_set_overlap_min']:.5f}")
+    assert st["steps"] == total
+    assert st["evictions_compared"] >= len(ds.units) * (total - w.C)
+    assert all(m <= 2e-2 for m in st["first_divergence_oracle_margins"]), st
+    diverged = set()
+    for u in range(len(ds.units)):
+        if np.any(ds.ev_gpu[:, u] != ds.ev_orc[:, u]):
+            diverged.add(u)
+    pos_g = ds.pos[ds.ub, ds.ug].cpu().numpy()
+    acc_g = ds.acc[ds.ub, ds.ug].cpu().numpy()
+    for u in range(len(ds.units)):
+        if u in diverged:
+            continue
+        np.testing.assert_array_equal(pos_g[u], ds.ost["pos"][u, 0])
+        assert rel_err(acc_g[u], ds.ost["acc"][u, 0], 1e-30).max() < 2e-2
+    if not diverged:
+        assert st["final_set_overlap_min"] == 1.0
