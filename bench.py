@@ -540,6 +540,9 @@ def main(argv=None):
                        dtype=torch.uint8, device="cuda")
     ws_r = torch.empty(max(256, hk.lib().hubkv_refine_workspace(w.B, sl, L, Hkv)),
                        dtype=torch.uint8, device="cuda")
+    ws_rs = torch.empty(hk.lib().hubkv_refine_select_workspace(w.B, sl, L, Hkv),
+                        dtype=torch.uint8, device="cuda")
+    fused = not args.layer_budget  # refine and select in one call (hubkv_refine_select)
     launch_stream = torch.cuda.current_stream()
 
     def step(ev=None, strm=None):
@@ -555,15 +558,22 @@ def main(argv=None):
             hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal, s=s, head_stats=st,
                            workspace=ws_s, stream=stream)
             if ev: ev[1].record(stream)
-            hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
-                            beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
-                            workspace=ws_r, stream=stream)
+            if fused:
+                hk.hubkv_refine_select(s, w.seqlens, kept, w.n_sink, w.n_recent, head_stats=st,
+                                       pool=w.pool, gamma=w.gamma, beta_lo=w.beta_lo,
+                                       beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta, idx=idx,
+                                       workspace=ws_rs, stream=stream)
+            else:
+                hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                                beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r, z=z, beta_out=beta,
+                                workspace=ws_r, stream=stream)
             if ev: ev[2].record(stream)
         if args.layer_budget:
             hk.hubkv_select_layer(z, w.seqlens, lk, w.n_sink, w.n_recent, floor, idx=idx_l,
                                   head_kept=hkept, workspace=ws_l, stream=stream)
-        else:
-            hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent, idx=idx, stream=stream)
+        elif not fused:
+            hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent, idx=idx, workspace=ws_rs,
+                            stream=stream)
         if ev: ev[3].record(stream)
         if args.layer_budget:
             hk.hubkv_compact_layer(Kd, Vd, idx_l, hkept, w.seqlens, lk, k_out=ko, v_out=vo,
@@ -607,6 +617,8 @@ def main(argv=None):
     names = ["score", "refine", "select", "compact"]
     op_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
              for j, n in enumerate(names)}
+    if fused:  # one call covers refinement and selection: one time for both
+        op_ms["refine_select"] = op_ms.pop("refine") + op_ms.pop("select")
     tokens = float(w.T * w.L)
     value = tokens / (ms_step / 1e3)
 
@@ -628,6 +640,7 @@ def main(argv=None):
                 "ranks": "16 .. N/16, layer 0, every KV head"}
 
     nb = op_bytes(w, Ksum, elem)
+    nb["refine_select"] = nb["refine"] + nb["select"]
     if args.nestedkv:
         nb["score"] = w.L * w.Hkv * w.T * (w.d * elem + 4)  # K read once, s written
     dom = max(op_ms, key=op_ms.get)
@@ -637,11 +650,12 @@ def main(argv=None):
         traffic = SCORE_TRAFFIC["fetch_bytes"] + SCORE_TRAFFIC["write_bytes"]
     ach = nb[dom] / (op_ms[dom] / 1e3) / 1e9
     rsc_bytes = nb["refine"] + nb["select"] + nb["compact"]
-    rsc_ms = op_ms["refine"] + op_ms["select"] + op_ms["compact"]
+    rsc_ms = sum(op_ms[k] for k in op_ms if k != "score")
     mfma_util = score_flops(w) / (op_ms["score"] / 1e3) / (BF16_PEAK_TFLOPS * 1e12)
     kernels = {"score": "score_pass_mfma<1> (row partials) + score_pass_mfma<2> (fold, column sums)" if elem == 2 else
                "score_stats_f32 + score_combine + score_probs_f32 + stats_final",
                "refine": "refine_kernel",
+               "refine_select": "msel_prep<refine> + msel_hist + msel_emit",
                "select": ("lsel_init + lsel_floor_level<0..2> + lsel_pool_level<0..2> + lsel_count"
                           " + lsel_emit_count + lsel_emit") if args.layer_budget else "select_kernel",
                "compact": "compact_layer_kernel" if args.layer_budget else "compact_kernel"}

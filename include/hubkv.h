@@ -6,6 +6,7 @@
  *   hubkv_score    base scores: attention mass of an observation window
  *   hubkv_refine   HubKV refinement of those scores before Top-K
  *   hubkv_select   per-head Top-K with protected sink and recent tokens
+ *   hubkv_refine_select  the two in one call
  *   hubkv_compact  gather of the kept K/V rows into a packed cache
  *   hubkv_score_strided / hubkv_compact_strided
  *                  the same on caller-strided views (token-major, padded)
@@ -177,6 +178,9 @@ int hubkv_refine(const float* s, int B, const int64_t* seqlens /* host */, int L
                  float* beta_out /* nullable */, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* Workspace bytes hubkv_select needs (0 on invalid sizes). */
+size_t hubkv_select_workspace(int B, const int64_t* seqlens /* host [B] */, int L, int Hkv);
+
 /*
  * hubkv_select -- per-head Top-K with protected windows.
  *
@@ -188,12 +192,34 @@ int hubkv_refine(const float* s, int B, const int64_t* seqlens /* host */, int L
  * protected positions plus the kept[b] - |protected| unprotected positions
  * with the largest z, ties to the lower position, NaN lowest, -0 == +0.  The
  * set is written ascending to idx at offset sum_{b' < b} kept[b'].
- * kept: host [B], |protected_b| <= kept[b] <= N_b.  The result is
- * deterministic.
+ * kept: host [B], |protected_b| <= kept[b] <= N_b.  workspace: at least
+ * hubkv_select_workspace() bytes, 256-byte aligned (scratch of the call; its
+ * content before the call does not matter).  The result is deterministic.
  */
 int hubkv_select(const float* z, int B, const int64_t* seqlens /* host */, int L, int Hkv,
                  const int64_t* kept /* host [B] */, int n_sink, int n_recent, int32_t* idx,
-                 void* stream);
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes hubkv_refine_select needs (0 on invalid sizes). */
+size_t hubkv_refine_select_workspace(int B, const int64_t* seqlens /* host [B] */, int L,
+                                     int Hkv);
+
+/*
+ * hubkv_refine_select -- hubkv_refine followed by hubkv_select in one call
+ * (HubKV walkthrough, "Method": the correction sits between the scorer and an
+ * unchanged Top-K).  Arguments as for the two calls; z (required) receives
+ * the refined scores and beta_out (nullable) the head weights.  Results
+ * equal those of hubkv_refine then hubkv_select bit for bit; the refinement
+ * runs inside the selection's first pass.  workspace: at least
+ * hubkv_refine_select_workspace() bytes, 256-byte aligned.
+ */
+int hubkv_refine_select(const float* s, int B, const int64_t* seqlens /* host */, int L, int Hkv,
+                        const double* head_stats /* nullable */,
+                        const float* beta_in /* nullable */, int pool, float gamma,
+                        float beta_lo, float beta_hi, float r, float* z,
+                        float* beta_out /* nullable */, const int64_t* kept /* host [B] */,
+                        int n_sink, int n_recent, int32_t* idx, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * hubkv_compact -- physically drop evicted tokens (H2O breakdown page, "two

@@ -132,14 +132,42 @@ def test_select_validation():
     L = hk.lib()
     sl = a64([100, 50])
 
-    def call(kept, ns=4, nr=16, z=P, idx=P + 4096, B=2, s=sl):
-        return L.hubkv_select(z, B, s, 1, 2, a64(kept), ns, nr, idx, None)
+    def call(kept, ns=4, nr=16, z=P, idx=P + 4096, B=2, s=sl, ws=P, wsb=1 << 30):
+        return L.hubkv_select(z, B, s, 1, 2, a64(kept), ns, nr, idx, ws, wsb, None)
 
     assert call([10, 30]) == EINVAL    # fewer than the 20 protected tokens
     assert call([30, 51]) == EINVAL    # more than the sequence
     assert call([30, 30], ns=-1) == EINVAL
     assert call([30, 30], z=None) == EALIGN
     assert call([30, 30], idx=P + 2) == EALIGN
+    assert call([30, 30], ws=None) == EWS
+    assert call([30, 30], wsb=16) == EWS
+    assert call([30, 30], ws=P + 8) == EALIGN
+    nb = L.hubkv_select_workspace(2, sl, 1, 2)
+    assert nb > 0 and call([30, 30], wsb=nb - 1) == EWS
+
+
+def test_refine_select_validation():
+    L = hk.lib()
+    sl = a64([100, 50])
+
+    def call(kept=(30, 30), pool=5, gamma=0.5, r=0.1, s=P, z=P + (1 << 20), idx=P + (1 << 21),
+             ws=P + (1 << 22), wsb=1 << 30, lo=0.8, hi=1.2):
+        return L.hubkv_refine_select(s, 2, sl, 1, 2, None, None, pool, gamma, lo, hi, r, z, None,
+                                     a64(list(kept)), 4, 16, idx, ws, wsb, None)
+
+    assert call(kept=(10, 30)) == EINVAL
+    assert call(pool=4) == EINVAL
+    assert call(gamma=0.0) == EINVAL
+    assert call(r=1.5) == EINVAL
+    assert call(lo=1.3) == EINVAL
+    assert call(z=P + 400) == EINVAL     # z overlaps s
+    assert call(z=None) == EALIGN
+    assert call(idx=P + (1 << 21) + 2) == EALIGN
+    assert call(wsb=8) == EWS
+    nb = L.hubkv_refine_select_workspace(2, sl, 1, 2)
+    assert nb >= L.hubkv_select_workspace(2, sl, 1, 2)
+    assert call(wsb=nb - 1) == EWS
 
 
 def test_compact_validation():
@@ -295,7 +323,7 @@ def test_sequence_length_limit():
     for n in ((1 << 30), (1 << 31) - 10, (1 << 31) - 1):
         sl = a64([n])
         kept = a64([n // 2])
-        assert L.hubkv_select(P, 1, sl, 1, 1, kept, 0, 0, P, None) == EINVAL
+        assert L.hubkv_select(P, 1, sl, 1, 1, kept, 0, 0, P, P, 1 << 40, None) == EINVAL
         assert L.hubkv_refine(P, 1, sl, 1, 1, None, None, 5, 0.5, 0.8, 1.2, 0.1, P + (1 << 40),
                               None, P, 1 << 40, None) == EINVAL
         assert L.hubkv_compact(P, P, 1, P, 1, sl, kept, 1, 1, 128, P, P, None) == EINVAL

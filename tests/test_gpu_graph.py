@@ -66,15 +66,18 @@ def test_prefill_chain_graph_replays_match_eager(G, W):
                        dtype=torch.uint8, **dev)
     ws_r = torch.empty(max(256, hk.lib().hubkv_refine_workspace(len(seqlens), sl, L, Hkv)),
                        dtype=torch.uint8, **dev)
+    ws_q = torch.empty(hk.lib().hubkv_select_workspace(len(seqlens), sl, L, Hkv),
+                       dtype=torch.uint8, **dev)
     ws_s.fill_(255)
     ws_r.fill_(255)
+    ws_q.fill_(255)
 
     def chain(o, strm):
         hk.hubkv_score(Qd, Kd, seqlens, W, scale, True, s=o["s"], head_stats=o["st"],
                        workspace=ws_s, stream=strm)
         hk.hubkv_refine(o["s"], seqlens, head_stats=o["st"], r=0.15, z=o["z"],
                         beta_out=o["beta"], workspace=ws_r, stream=strm)
-        hk.hubkv_select(o["z"], seqlens, kept, 4, 32, idx=o["idx"], stream=strm)
+        hk.hubkv_select(o["z"], seqlens, kept, 4, 32, idx=o["idx"], workspace=ws_q, stream=strm)
         hk.hubkv_compact(Kd, Vd, o["idx"], seqlens, kept, k_out=o["ko"], v_out=o["vo"],
                          stream=strm)
 

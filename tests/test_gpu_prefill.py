@@ -173,6 +173,9 @@ SELECT_CASES = [
     ([491520, 4099], 1, 1, None, 0, 64, "bin8000"),   # a planted bin just under the cap, ragged
     ([600001], 1, 1, 0.1, 4, 128, "attention"),       # past 16 rounds: the general path
     ([540000, 7], 1, 1, 0.05, 0, 64, "special"),      # general path, long, NaN / signs / inf
+    # over 1024 slices of 4096 positions in one call: the 256-thread work-groups
+    ([400000, 300000, 200001, 150000], 2, 2, 0.1, 4, 64, "special"),
+    ([400000, 300000, 200001, 150000], 2, 2, 0.1, 4, 64, "ties"),
 ]
 
 
@@ -229,6 +232,83 @@ def test_select_bitexact_given_scores(case):
     np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
 
 
+# ------------------------------------------------------- refine + select ---
+RSEL_CASES = [
+    # seqlens, L, Hkv, kind, ties, pool, gamma, r, budget, n_sink, n_recent
+    ([1000], 1, 4, "attention", False, 5, 0.5, 0.2, 0.2, 0, 16),
+    ([3000, 517, 9000], 2, 3, "attention", True, 5, 0.5, 0.1, 0.1, 4, 64),
+    ([4096, 4097, 8191], 1, 2, "attention", False, 5, 0.5, 0.1, 0.1, 4, 64),  # slice edges
+    ([2049], 1, 2, "uniform", False, 3, 0.5, 1.0, 0.3, 2, 8),
+    ([40000, 777], 1, 2, "attention", True, 7, 0.75, 0.05, 0.05, 4, 128),
+    ([32768], 1, 8, "attention", False, 5, 0.5, 0.1, 0.1, 4, 64),
+    ([131072, 5], 1, 2, "attention", False, 5, 0.5, 0.1, 0.1, 4, 64),       # a 5-token sequence
+    ([200000, 99999, 3], 2, 8, "attention", True, 5, 0.5, 0.1, 0.1, 4, 64),  # 1200 slices
+]
+
+
+@pytest.mark.parametrize("case", RSEL_CASES, ids=lambda c: f"T{sum(c[0])}-{c[3]}-ties{int(c[4])}-p{c[5]}")
+def test_refine_select_bitexact(case):
+    """The fused call: z bit-exact with the oracle's refinement given the same
+    s and beta, the kept set bit-exact with the oracle's selection of that z;
+    with beta from statistics, beta within 1e-6 and the outputs bit-exact
+    with the oracle run on the GPU's own beta."""
+    seqlens, L, Hkv, kind, ties, pool, gamma, r, budget, ns, nr = case
+    s = S.random_scores(seqlens, L, Hkv, seed=3 + sum(seqlens), kind=kind, ties=ties)
+    st = oracle.head_stats(s, seqlens)
+    beta = oracle.beta(st, seqlens)
+    kept = np.maximum(S.budgets(seqlens, budget),
+                      [oracle.protected_count(n, ns, nr) for n in seqlens])
+    sd = to_dev(s, "f32")
+    for mode in ("beta_in", "stats", "none"):
+        z_g, b_g, idx_g = hk.hubkv_refine_select(
+            sd, seqlens, kept, ns, nr, pool=pool, gamma=gamma, r=r,
+            beta_in=to_dev(beta, "f32") if mode == "beta_in" else None,
+            head_stats=torch.from_numpy(st).cuda() if mode == "stats" else None)
+        torch.cuda.synchronize()
+        z_g, b_g, idx_g = z_g.cpu().numpy(), b_g.cpu().numpy(), idx_g.cpu().numpy()
+        if mode == "beta_in":
+            np.testing.assert_array_equal(b_g, beta)
+        else:
+            assert rel_err(b_g, beta).max() < 1e-6
+        np.testing.assert_array_equal(z_g, oracle.refine(s, seqlens, b_g, pool, gamma, r))
+        np.testing.assert_array_equal(idx_g, oracle.select(z_g, seqlens, kept, ns, nr))
+
+
+def test_refine_select_equals_separate_calls_on_one_workspace():
+    """hubkv_refine_select equals hubkv_refine then hubkv_select, over calls
+    of different shapes that share one (poisoned) workspace."""
+    shapes = [([65536, 3000], 2, 4), ([5000], 1, 2), ([300, 4096, 12289], 1, 3)]
+    nb = max(hk.lib().hubkv_refine_select_workspace(len(sl), hk._arr64(sl), L, H)
+             for sl, L, H in shapes)
+    ws = torch.full((nb,), 255, dtype=torch.uint8, device="cuda")
+    for i, (seqlens, L, Hkv) in enumerate(shapes):
+        s = S.random_scores(seqlens, L, Hkv, seed=40 + i, ties=(i == 1))
+        kept = np.maximum(S.budgets(seqlens, 0.15),
+                          [oracle.protected_count(n, 4, 32) for n in seqlens])
+        sd = to_dev(s, "f32")
+        st = torch.from_numpy(oracle.head_stats(s, seqlens)).cuda()
+        z1, b1, i1 = hk.hubkv_refine_select(sd, seqlens, kept, 4, 32, head_stats=st, r=0.2,
+                                            workspace=ws)
+        z2, b2 = hk.hubkv_refine(sd, seqlens, head_stats=st, r=0.2)
+        i2 = hk.hubkv_select(z2, seqlens, kept, 4, 32, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(z1, z2) and torch.equal(b1, b2) and torch.equal(i1, i2), i
+
+
+@pytest.mark.parametrize("n", [4194304, 4194305])
+def test_select_longest_sequences(n):
+    """4194304 positions (1024 slices of 4096, the most the many-work-group
+    select takes) and one more (the one-work-group select), bit-exact."""
+    seqlens = [n, 1000]
+    z = S.random_scores(seqlens, 1, 1, seed=n % 1000, kind="attention", ties=True)
+    kept = np.maximum(S.budgets(seqlens, 0.1),
+                      [oracle.protected_count(x, 4, 128) for x in seqlens])
+    idx_o = oracle.select(z, seqlens, kept, 4, 128)
+    idx_g = hk.hubkv_select(to_dev(z, "f32"), seqlens, kept, 4, 128)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
+
+
 # ---------------------------------------------------------------- compact ---
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_compact_bitexact_given_indices(dtype, d):
@@ -253,14 +333,22 @@ def test_compact_bitexact_given_indices(dtype, d):
 
 # ------------------------------------------------------------ whole chain ---
 def _gpu_chain(Q, K, V, w, budget=None, r=None):
+    # the chain as the benchmark runs it (refinement and selection in one
+    # call), and the two separate calls, which must agree bit for bit
     kept = w.kept(budget)
+    rr = w.r if r is None else r
     Qd, Kd, Vd = to_dev(Q, w.dtype), to_dev(K, w.dtype), to_dev(V, w.dtype)
     s, st = hk.hubkv_score(Qd, Kd, w.seqlens, w.W, w.scale, w.causal)
-    z, beta = hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
-                              beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=w.r if r is None else r)
-    idx = hk.hubkv_select(z, w.seqlens, kept, w.n_sink, w.n_recent)
+    z, beta, idx = hk.hubkv_refine_select(s, w.seqlens, kept, w.n_sink, w.n_recent,
+                                          head_stats=st, pool=w.pool, gamma=w.gamma,
+                                          beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=rr)
+    z2, beta2 = hk.hubkv_refine(s, w.seqlens, head_stats=st, pool=w.pool, gamma=w.gamma,
+                                beta_lo=w.beta_lo, beta_hi=w.beta_hi, r=rr)
+    idx2 = hk.hubkv_select(z2, w.seqlens, kept, w.n_sink, w.n_recent)
     ko, vo = hk.hubkv_compact(Kd, Vd, idx, w.seqlens, kept)
     torch.cuda.synchronize()
+    assert torch.equal(z, z2) and torch.equal(beta, beta2) and torch.equal(idx, idx2)
+    del z2, beta2, idx2
     return dict(s=s.cpu().numpy(), stats=st.cpu().numpy(), beta=beta.cpu().numpy(),
                 z=z.cpu().numpy(), idx=idx.cpu().numpy(), k_out=to_host(ko), v_out=to_host(vo),
                 kept=kept)

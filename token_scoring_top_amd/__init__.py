@@ -14,6 +14,7 @@ Functions (names follow the C ABI):
     hubkv_score_noalloc(q, k, seqlens, W, scale, ...)  -> (s, head_stats), no workspace
     hubkv_refine(s, seqlens, ...)                      -> (z, beta)
     hubkv_select(z, seqlens, kept, n_sink, n_recent)   -> idx
+    hubkv_refine_select(s, seqlens, kept, n_sink, n_recent, ...) -> (z, beta, idx)
     hubkv_compact(k, v, idx, seqlens, kept)            -> (k_out, v_out)
     (q, k, v and the compaction outputs may be strided views whose last
      axis is contiguous: those calls go to hubkv_score_strided and
@@ -61,7 +62,11 @@ _SIGS = {
     "hubkv_refine_workspace": (_sz, [_i, _i64p, _i, _i]),
     "hubkv_refine": (_i, [_vp, _i, _i64p, _i, _i, _vp, _vp, _i, _f, _f, _f, _f, _vp, _vp, _vp, _sz,
                           _vp]),
-    "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp]),
+    "hubkv_select_workspace": (_sz, [_i, _i64p, _i, _i]),
+    "hubkv_select": (_i, [_vp, _i, _i64p, _i, _i, _i64p, _i, _i, _vp, _vp, _sz, _vp]),
+    "hubkv_refine_select_workspace": (_sz, [_i, _i64p, _i, _i]),
+    "hubkv_refine_select": (_i, [_vp, _i, _i64p, _i, _i, _vp, _vp, _i, _f, _f, _f, _f, _vp, _vp,
+                                 _i64p, _i, _i, _vp, _vp, _sz, _vp]),
     "hubkv_compact": (_i, [_vp, _vp, _i, _vp, _i, _i64p, _i64p, _i, _i, _i, _vp, _vp, _vp]),
     "hubkv_score_noalloc": (_i, [_vp, _vp, _i, _i, _i64p, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                  _vp]),
@@ -288,18 +293,50 @@ def hubkv_refine(s, seqlens: Sequence[int], head_stats=None, beta_in=None, pool:
 
 
 def hubkv_select(z, seqlens: Sequence[int], kept: Sequence[int], n_sink: int, n_recent: int,
-                 idx=None, stream=None):
+                 idx=None, workspace=None, stream=None):
     """z fp32 [L][Hkv][T] -> idx int32 [L][Hkv][sum kept] (ascending per sequence)."""
     torch = _torch()
     L, Hkv, T = z.shape
     B = len(seqlens)
+    sl = _arr64(seqlens)
     with _on(stream):
         if idx is None:
             idx = _new((L, Hkv, int(sum(kept))), torch.int32, z.device)
-        _check("hubkv_select", lib().hubkv_select(_ptr(z), B, _arr64(seqlens), L, Hkv,
-                                                  _arr64(kept), int(n_sink), int(n_recent),
-                                                  _ptr(idx), _stream(stream)))
+        if workspace is None:
+            workspace = _workspace(lib().hubkv_select_workspace(B, sl, L, Hkv), z.device)
+        _check("hubkv_select", lib().hubkv_select(_ptr(z), B, sl, L, Hkv, _arr64(kept),
+                                                  int(n_sink), int(n_recent), _ptr(idx),
+                                                  _ptr(workspace), workspace.numel(),
+                                                  _stream(stream)))
     return idx
+
+
+def hubkv_refine_select(s, seqlens: Sequence[int], kept: Sequence[int], n_sink: int,
+                        n_recent: int, head_stats=None, beta_in=None, pool: int = 5,
+                        gamma: float = 0.5, beta_lo: float = 0.8, beta_hi: float = 1.2,
+                        r: float = 0.1, z=None, beta_out=None, idx=None, workspace=None,
+                        stream=None):
+    """hubkv_refine then hubkv_select in one call: s fp32 [L][Hkv][T] ->
+    (z fp32 [L][Hkv][T], beta fp32 [L][B][Hkv], idx int32 [L][Hkv][sum kept])."""
+    torch = _torch()
+    L, Hkv, T = s.shape
+    B = len(seqlens)
+    sl = _arr64(seqlens)
+    with _on(stream):
+        if z is None:
+            z = _new((L, Hkv, T), torch.float32, s.device)
+        if beta_out is None:
+            beta_out = _new((L, B, Hkv), torch.float32, s.device)
+        if idx is None:
+            idx = _new((L, Hkv, int(sum(kept))), torch.int32, s.device)
+        if workspace is None:
+            workspace = _workspace(lib().hubkv_refine_select_workspace(B, sl, L, Hkv), s.device)
+        _check("hubkv_refine_select", lib().hubkv_refine_select(
+            _ptr(s), B, sl, L, Hkv, _ptr(head_stats), _ptr(beta_in), int(pool), float(gamma),
+            float(beta_lo), float(beta_hi), float(r), _ptr(z), _ptr(beta_out), _arr64(kept),
+            int(n_sink), int(n_recent), _ptr(idx), _ptr(workspace), workspace.numel(),
+            _stream(stream)))
+    return z, beta_out, idx
 
 
 def hubkv_compact(k_in, v_in, idx, seqlens: Sequence[int], kept: Sequence[int], k_out=None,

@@ -424,15 +424,98 @@ int hubkv_refine(const float* s, int B, const int64_t* seqlens, int L, int Hkv,
                                   z, beta_out, strm));
 }
 
-int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
-                 const int64_t* kept, int n_sink, int n_recent, int32_t* idx, void* stream) {
+// The many-work-group select covers sequences of up to kMsSlice x
+// kMsMaxSlices positions; a call with a longer sequence uses the
+// one-work-group select for all of its units.
+static bool msel_fits(const SeqTable& st) {
+  for (int b = 0; b < st.B; ++b)
+    if (st.N[b] > (int64_t)kMsSlice * kMsMaxSlices) return false;
+  return true;
+}
+
+size_t hubkv_select_workspace(int B, const int64_t* seqlens, int L, int Hkv) {
   SeqTable st;
-  int rc = make_table(st, B, seqlens, kRefineTile);
+  if (make_table(st, B, seqlens, kMsSlice) != HUBKV_OK) return 0;
+  if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return 0;
+  if (!msel_fits(st)) return 256;  // the one-work-group select needs no workspace
+  return msel_geometry(st, L, Hkv).bytes;
+}
+
+int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
+                 const int64_t* kept, int n_sink, int n_recent, int32_t* idx, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  SeqTable st;
+  int rc = make_table(st, B, seqlens, kMsSlice);
   if (rc) return rc;
   if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
   if ((rc = check_kept(st, kept, n_sink, n_recent, true))) return rc;
   if (!z || !idx || !aligned(z, 4) || !aligned(idx, 4)) return HUBKV_EALIGN;
-  return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, (hipStream_t)stream));
+  if (!msel_fits(st))
+    return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, (hipStream_t)stream));
+  const MselGeom geo = msel_geometry(st, L, Hkv);
+  if (!workspace || workspace_bytes < geo.bytes) return HUBKV_EWORKSPACE;
+  if (!aligned(workspace, 256)) return HUBKV_EALIGN;
+  const RefineParams rp{};
+  return hip_status(launch_msel(z, false, nullptr, st, L, Hkv, n_sink, n_recent, rp, idx,
+                                (char*)workspace, geo, (hipStream_t)stream));
+}
+
+size_t hubkv_refine_select_workspace(int B, const int64_t* seqlens, int L, int Hkv) {
+  const size_t r = hubkv_refine_workspace(B, seqlens, L, Hkv);
+  const size_t q = hubkv_select_workspace(B, seqlens, L, Hkv);
+  if (!r || !q) return 0;
+  return ((r + 255) & ~(size_t)255) + q;
+}
+
+int hubkv_refine_select(const float* s, int B, const int64_t* seqlens, int L, int Hkv,
+                        const double* head_stats, const float* beta_in, int pool, float gamma,
+                        float beta_lo, float beta_hi, float r, float* z, float* beta_out,
+                        const int64_t* kept, int n_sink, int n_recent, int32_t* idx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  SeqTable rt, st;
+  int rc = make_table(rt, B, seqlens, kRefineTile);
+  if (rc) return rc;
+  if ((rc = make_table(st, B, seqlens, kMsSlice))) return rc;
+  if (L < 1 || Hkv < 1 || Hkv > 1024 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
+  if (pool < 1 || pool % 2 == 0 || pool > 63) return HUBKV_EINVAL;
+  if (!(gamma > 0.f && gamma <= 1.f)) return HUBKV_EINVAL;
+  if (!(isfinite(beta_lo) && isfinite(beta_hi) && beta_lo <= beta_hi)) return HUBKV_EINVAL;
+  if (!(r >= 0.f && r <= 1.f)) return HUBKV_EINVAL;
+  if ((rc = check_kept(st, kept, n_sink, n_recent, true))) return rc;
+  if (!s || !z || !idx || !aligned(s, 4) || !aligned(z, 4) || !aligned(idx, 4))
+    return HUBKV_EALIGN;
+  if ((head_stats && !aligned(head_stats, 8)) || (beta_in && !aligned(beta_in, 4)) ||
+      (beta_out && !aligned(beta_out, 4)))
+    return HUBKV_EALIGN;
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) T += st.N[b];
+  const uintptr_t n = (uintptr_t)((int64_t)L * Hkv * T) * sizeof(float);
+  if ((uintptr_t)s < (uintptr_t)z + n && (uintptr_t)z < (uintptr_t)s + n) return HUBKV_EINVAL;
+  const RefineGeom rg = refine_geometry(rt, L, Hkv);
+  const size_t roff = (rg.bytes + 255) & ~(size_t)255;
+  const bool many = msel_fits(st);
+  const MselGeom geo = many ? msel_geometry(st, L, Hkv) : MselGeom{};
+  if (!workspace || workspace_bytes < roff + (many ? geo.bytes : 256)) return HUBKV_EWORKSPACE;
+  if (!aligned(workspace, 256)) return HUBKV_EALIGN;
+  char* ws = (char*)workspace;
+  hipStream_t strm = (hipStream_t)stream;
+  const double* stats = head_stats;
+  if (!beta_in && !stats) {
+    double* st_ws = (double*)(ws + rg.off_stats);
+    rc = hip_status(launch_head_stats(s, rt, L, Hkv, (double*)(ws + rg.off_part), st_ws, strm));
+    if (rc) return rc;
+    stats = st_ws;
+  }
+  const float r2 = r * r;  // fp32 product, as the gate formula is evaluated in fp32
+  if (!many) {
+    rc = hip_status(launch_refine(s, rt, L, Hkv, stats, beta_in, pool, gamma, beta_lo, beta_hi,
+                                  r2, z, beta_out, strm));
+    if (rc) return rc;
+    return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, strm));
+  }
+  const RefineParams rp{pool, gamma, r2, beta_lo, beta_hi, beta_in, stats, beta_out};
+  return hip_status(launch_msel(s, true, z, st, L, Hkv, n_sink, n_recent, rp, idx, ws + roff, geo,
+                                strm));
 }
 
 int hubkv_compact_strided(const void* k_in, const int64_t* k_in_strides, const void* v_in,

@@ -101,6 +101,49 @@ hipError_t launch_refine(const float* s, const SeqTable& st, int L, int Hkv,
 hipError_t launch_select(const float* z, const SeqTable& st, int L, int Hkv, int n_sink,
                          int n_recent, int32_t* idx, hipStream_t stream);
 
+// ---- protected Top-K over many work-groups per unit ---------------------------
+constexpr int kMsSlice = 4096;       // positions per work-group (the table's tile)
+constexpr int kMsMaxSlices = 1024;   // slices per sequence: sequences up to 4M positions
+
+struct MselGeomDev {
+  size_t off_head, off_pre, off_sorted;
+};
+struct MselGeom {
+  MselGeomDev d;
+  size_t bytes;
+};
+
+// Kernel-argument block of the many-work-group select (and its fused
+// refinement); st is cut into kMsSlice-position tiles and carries kept/ko.
+struct MselArgs {
+  SeqTable st;
+  int Hkv, n_sink, n_recent, nslice;
+  int max_nsl;  // slices of the longest sequence
+  int64_t T, Ktot;
+  MselGeomDev g;
+  int half;
+  float gamma, r2, beta_lo, beta_hi;
+  const float* beta_in;
+  const double* stats;
+  float* beta_out;
+};
+
+struct RefineParams {
+  int pool;
+  float gamma, r2, beta_lo, beta_hi;
+  const float* beta_in;
+  const double* stats;
+  float* beta_out;
+};
+
+MselGeom msel_geometry(const SeqTable& st, int L, int Hkv);
+
+// Select on z (refine = false: src is z), or refine s into z and select
+// (refine = true: src is s, z receives the refined scores).
+hipError_t launch_msel(const float* src, bool refine, float* z, const SeqTable& st, int L,
+                       int Hkv, int n_sink, int n_recent, const RefineParams& rp, int32_t* idx,
+                       char* ws, const MselGeom& geo, hipStream_t stream);
+
 // ---- layer-wide budget --------------------------------------------------------------
 constexpr int kMaxLayerSegs = 256;  // (layer, sequence) pairs per call
 constexpr int kLselChunk = 4096;    // positions per work-group

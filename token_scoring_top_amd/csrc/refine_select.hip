@@ -141,6 +141,33 @@ __device__ __forceinline__ float smd_gate(float si, bool hub, float gamma, float
   return __builtin_fmaf(r2, d, si);
 }
 
+// Refined score of position i (tile-local index j) of a sequence of N
+// positions whose tile starts at i0: tile[j + half] holds s_i and the halo
+// sits on both sides.  The window maximum is scanned from its lowest
+// in-sequence position upwards with a strict compare, so that a NaN first
+// entry stays the maximum as in a plain scan.
+__device__ __forceinline__ float refined(const float* tile, int j, int i, int i0, int N, int half,
+                                         float gamma, float bt, float r2) {
+  const float si = tile[j + half];
+  float mx;
+  if (half == 2 && i >= 2 && i + 2 < N) {
+    mx = tile[j];
+    mx = tile[j + 1] > mx ? tile[j + 1] : mx;
+    mx = si > mx ? si : mx;
+    mx = tile[j + 3] > mx ? tile[j + 3] : mx;
+    mx = tile[j + 4] > mx ? tile[j + 4] : mx;
+  } else {
+    const int wlo = i - half < 0 ? 0 : i - half;
+    const int whi = i + half > N - 1 ? N - 1 : i + half;
+    mx = tile[wlo - i0 + half];
+    for (int k = wlo + 1; k <= whi; ++k) {
+      const float v = tile[k - i0 + half];
+      mx = v > mx ? v : mx;
+    }
+  }
+  return smd_gate(si, si == mx, gamma, bt, r2);
+}
+
 __global__ __launch_bounds__(kRefineThreads) void refine_kernel(
     const float* __restrict__ s, SeqTable st, int64_t T, int Hkv, int half, float gamma, float r2,
     const float* __restrict__ beta_in, const double* __restrict__ stats, float lo, float hi,
@@ -183,29 +210,10 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(
   }
   __syncthreads();
   const float bt = sh_beta;
-  // window max scanned from its lowest in-sequence position upwards with a
-  // strict compare, so that a NaN first entry stays the max as in a plain scan
   for (int j = threadIdx.x; j < kRefineTile; j += kRefineThreads) {
     const int i = i0 + j;
     if (i >= N) break;
-    const float si = tile[j + half];
-    float mx;
-    if (half == 2 && i >= 2 && i + 2 < N) {
-      mx = tile[j];
-      mx = tile[j + 1] > mx ? tile[j + 1] : mx;
-      mx = si > mx ? si : mx;
-      mx = tile[j + 3] > mx ? tile[j + 3] : mx;
-      mx = tile[j + 4] > mx ? tile[j + 4] : mx;
-    } else {
-      const int wlo = i - half < 0 ? 0 : i - half;
-      const int whi = i + half > N - 1 ? N - 1 : i + half;
-      mx = tile[wlo - i0 + half];
-      for (int k = wlo + 1; k <= whi; ++k) {
-        const float v = tile[k - i0 + half];
-        mx = v > mx ? v : mx;
-      }
-    }
-    zb[i] = smd_gate(si, si == mx, gamma, bt, r2);
+    zb[i] = refined(tile, j, i, i0, N, half, gamma, bt, r2);
   }
 }
 
@@ -398,7 +406,8 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t need, Se
 // Ordered writes of one round: keys above thr, then the first rem keys equal
 // to thr, ranked from D and Tt (keys above / equal to thr before this wave's
 // rows).  Keys in registers, specials applied.
-__device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool edge, uint32_t thr,
+template <int R>
+__device__ __forceinline__ void emit_round(const uint32_t (&key)[R], bool edge, uint32_t thr,
                                            uint32_t rem, uint32_t D, uint32_t Tt, int p0, int kept,
                                            int32_t* __restrict__ out) {
   uint32_t thw = thr;
@@ -407,11 +416,11 @@ __device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool 
   // stays put and each row needs one ballot
   bool anyeq = false;
 #pragma unroll
-  for (int j = 0; j < kSelKpt; ++j) anyeq |= key[j] == thw;
+  for (int j = 0; j < R; ++j) anyeq |= key[j] == thw;
   if (!__any(anyeq)) {
     uint32_t base = D + (Tt < rem ? Tt : rem);
 #pragma unroll
-    for (int j = 0; j < kSelKpt; ++j) {
+    for (int j = 0; j < R; ++j) {
       const uint32_t k = key[j];
       const bool def = edge ? (k > thw && k != kPad) : (k > thw);
       const unsigned long long bd = __ballot(def);
@@ -422,7 +431,7 @@ __device__ __forceinline__ void emit_round(const uint32_t (&key)[kSelKpt], bool 
     return;
   }
 #pragma unroll
-  for (int j = 0; j < kSelKpt; ++j) {
+  for (int j = 0; j < R; ++j) {
     const uint32_t k = key[j];
     const bool def = edge ? (k > thw && k != kPad) : (k > thw);
     const unsigned long long bd = __ballot(def);
@@ -835,6 +844,530 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Protected Top-K over many work-groups per (layer, KV head, sequence) unit.
+//
+// Every sequence is cut into slices of kMsSlice positions, one 256-thread
+// work-group per (layer-head, slice), so a unit is spread over ceil(N /
+// kMsSlice) compute units.  Two launches; no work-group waits for another:
+//   bin   z of the slice (the refinement fused in, or read from z) and the
+//         order-preserving 32-bit key of every unprotected position.  Keys go
+//         to 4096 bins of 2^14 key units (1/512 of an octave for normal
+//         floats) placed around an estimate of the unit's threshold, the
+//         outermost bins catching everything beyond; the estimate is the
+//         matching quantile of 64 sample positions spread over the unit,
+//         which every slice reads and sorts alike, so all slices bin the same
+//         way without talking.  The slice stores its bins' starts, 64 coarse
+//         counts (64 bins each) and its keys' low bits and positions sorted by
+//         bin.
+//   pick  every slice of the unit finds, redundantly, the coarse bin, then
+//         the bin, holding the k-th largest unprotected key (from all slices'
+//         coarse counts and bin starts), gathers that bin's keys from all
+//         slices' sorted lists, resolves the exact threshold key and how many
+//         of its ties are kept (radix passes over the gathered keys), counts
+//         the kept keys of the slices before it, and writes its own kept
+//         positions (protected ones included), ranked with ballots.
+// Bins, thresholds and counts are integers computed identically in every
+// slice, so the result equals the one-work-group select bit for bit and does
+// not depend on timing.  A bin with more keys than the LDS list holds is
+// resolved by streaming its keys from memory on every pass (exact, slower).
+// ---------------------------------------------------------------------------
+// work-group size: 1024 threads (16 waves, 4 rows of 64 positions each) when
+// the grid is small enough to leave compute units idle, 256 threads (4 waves,
+// 16 rows each) when many slices keep every compute unit busy
+constexpr int kMsBigGrid = 1024;  // slices per launch from which 256-thread work-groups are used
+constexpr int kMsBins = 4096;
+constexpr int kMsShift = 14;                    // bin width in key units
+constexpr int kMsCoarse = 64;                   // coarse bins (of 64 bins each)
+constexpr int kMsListCap = 4096;                // threshold-bin keys held in LDS
+constexpr uint32_t kNoneKept = 0xfffffffdu;     // threshold above every unprotected key
+
+struct MselHead {     // per (layer-head, slice); 256 bytes
+  uint32_t ncand;     // unprotected positions of the slice
+  int32_t kc;         // window centre, in key >> kMsShift units (the same in every slice)
+  uint32_t pad[30];
+  uint32_t coarse[kMsCoarse / 2];  // 16-bit coarse counts, packed pairs
+};
+
+struct MselPtrs {
+  MselHead* head;     // [L*Hkv][nslice]
+  uint32_t* pre;      // [L*Hkv][nslice][kMsBins / 2]: 16-bit bin starts, packed pairs
+  uint32_t* sorted;   // [L*Hkv][nslice][kMsSlice]: key low bits | slice position << 14
+};
+
+__device__ __forceinline__ MselPtrs msel_ptrs(char* ws, const MselGeomDev& g) {
+  return MselPtrs{(MselHead*)(ws + g.off_head), (uint32_t*)(ws + g.off_pre),
+                  (uint32_t*)(ws + g.off_sorted)};
+}
+
+// Protected window [0, a) U [c, N) of a sequence of N positions.
+__device__ __forceinline__ void prot_bounds(int N, int n_sink, int n_recent, int& a, int& c) {
+  a = n_sink < N ? n_sink : N;
+  c = N - n_recent > 0 ? N - n_recent : 0;
+  if (c < a) c = a;
+}
+
+// Bin of an order key in the window centred on kc (key >> kMsShift units).
+__device__ __forceinline__ int msel_bin_of(uint32_t key, int kc) {
+  const int d = (int)(key >> kMsShift) - kc + kMsBins / 2;
+  return d < 0 ? 0 : (d > kMsBins - 1 ? kMsBins - 1 : d);
+}
+
+// Ascending bitonic sort across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_sort_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t o = __shfl_xor(v, j);
+      const bool up = (lane & k) == 0 || k == 64;
+      const bool lower = (lane & j) == 0;
+      v = (lower == up) ? (o < v ? o : v) : (o > v ? o : v);
+    }
+  }
+  return v;
+}
+
+// 16-bit entry i of an array of packed pairs.
+__device__ __forceinline__ uint32_t ld16(const uint32_t* base, int i) {
+  const uint32_t w = base[i >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <bool REFINE, int kMsThreads>
+__global__ __launch_bounds__(kMsThreads) void msel_bin(const float* __restrict__ src,
+                                                       float* __restrict__ z, MselArgs a,
+                                                       char* __restrict__ ws) {
+  constexpr int kMsWaves = kMsThreads / 64;
+  constexpr int kMsRows = kMsSlice / kMsThreads;  // rows of 64 positions per wave
+  __shared__ float tile[REFINE ? kMsSlice + 2 * kMaxHalf : 1];
+  __shared__ uint32_t hist[kMsBins];         // counts, then scatter cursors
+  __shared__ uint32_t srt[kMsSlice];         // packed keys in bin order
+  __shared__ uint32_t wsum[kMsWaves];
+  __shared__ float sh_beta;
+  __shared__ int sh_kc;
+  const MselPtrs P = msel_ptrs(ws, a.g);
+  const int lh = blockIdx.y, x = blockIdx.x;
+  const int l = lh / a.Hkv, g = lh - l * a.Hkv;
+  const int b = seq_of_tile(a.st, x);
+  const int N = (int)a.st.N[b];
+  const int s0 = (x - a.st.tile_off[b]) * kMsSlice;
+  int A, Cc;
+  prot_bounds(N, a.n_sink, a.n_recent, A, Cc);
+  const int ncand_u = Cc - A;
+  const int need = (int)a.st.kept[b] - (N - ncand_u);  // unprotected positions kept
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p0 = s0 + wave * (64 * kMsRows) + lane;
+  const float* sb = src + (int64_t)lh * a.T + a.st.cu[b];
+  float v[kMsRows];
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    const int p = p0 + 64 * j;
+    v[j] = p < N ? sb[p] : 0.f;
+  }
+  // wave 0: the window centre from 64 sample positions of the unit's
+  // unprotected range (their scores before refinement when refining)
+  uint32_t samp = 0u;
+  if (wave == 0 && ncand_u > 0) {
+    const int ps = A + (int)(((int64_t)(2 * lane + 1) * ncand_u) / 128);
+    samp = order_key_bits(__float_as_uint(sb[ps]));
+  }
+  float hv = 0.f;
+  const int half = REFINE ? a.half : 0;
+  if (REFINE && tid < 2 * half) {
+    const int i = tid < half ? s0 - half + tid : s0 + kMsSlice - half + tid;
+    hv = (i >= 0 && i < N) ? sb[i] : 0.f;
+  }
+  for (int i = tid; i < kMsBins; i += kMsThreads) hist[i] = 0u;
+  if (wave == 0) {
+    samp = wave_sort_u32(samp, lane);
+    int q = ncand_u > 0 ? (int)(((int64_t)(ncand_u - need) * 64) / ncand_u) : 0;
+    q = q < 0 ? 0 : (q > 63 ? 63 : q);
+    const uint32_t kq = __shfl(samp, q);
+    if (lane == 0) sh_kc = (int)(kq >> kMsShift);
+  }
+  if constexpr (REFINE) {
+    float* zb = z + (int64_t)lh * a.T + a.st.cu[b];
+#pragma unroll
+    for (int j = 0; j < kMsRows; ++j) tile[half + p0 + 64 * j - s0] = v[j];
+    if (tid < 2 * half) tile[tid < half ? tid : kMsSlice + tid] = hv;
+    if (tid >= 64 && tid < 128) {  // wave 1: the head weight
+      const int lb = l * a.st.B + b;
+      const int u = lb * a.Hkv + g;
+      const float bt = a.beta_in ? a.beta_in[u]
+                                 : head_beta(a.st, lb, b, g, a.Hkv, a.stats, a.beta_lo, a.beta_hi);
+      if (tid == 64) {
+        sh_beta = bt;
+        if (a.beta_out && s0 == 0) a.beta_out[u] = bt;
+      }
+    }
+    __syncthreads();
+    const float bt = sh_beta;
+#pragma unroll
+    for (int j = 0; j < kMsRows; ++j) {
+      const int p = p0 + 64 * j;
+      if (p < N) {
+        v[j] = refined(tile, p - s0, p, s0, N, half, a.gamma, bt, a.r2);
+        zb[p] = v[j];
+      }
+    }
+  } else {
+    __syncthreads();
+  }
+  const int kc = sh_kc;
+  // bins of the slice's unprotected keys
+  uint32_t bin[kMsRows], low[kMsRows];
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    const int p = p0 + 64 * j;
+    const uint32_t k = order_key_bits(__float_as_uint(v[j]));
+    low[j] = k & ((1u << kMsShift) - 1u);
+    bin[j] = (p >= A && p < Cc) ? (uint32_t)msel_bin_of(k, kc) : 0xffffffffu;
+    if (bin[j] != 0xffffffffu) atomicAdd(&hist[bin[j]], 1u);
+  }
+  __syncthreads();
+  // this thread's 16 bins: exclusive starts (the scatter cursors), published
+  constexpr int PER = kMsBins / kMsThreads;
+  uint32_t h[PER], tot = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    h[e] = hist[tid * PER + e];
+    tot += h[e];
+  }
+  uint32_t incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t start = incl - tot;
+  for (int w = 0; w < wave; ++w) start += wsum[w];
+  const int64_t sl = (int64_t)lh * a.nslice + x;
+  uint32_t* pre = P.pre + sl * (kMsBins / 2);
+#pragma unroll
+  for (int e = 0; e < PER; e += 2) {
+    const uint32_t s_e = start, s_f = start + h[e];
+    pre[(tid * PER + e) >> 1] = s_e | (s_f << 16);
+    hist[tid * PER + e] = s_e;
+    hist[tid * PER + e + 1] = s_f;
+    start = s_f + h[e + 1];
+  }
+  // coarse counts: TPC threads per coarse bin of 64 bins, two bins a word
+  constexpr int TPC = 64 / PER;
+  uint32_t cq = tot;
+#pragma unroll
+  for (int off = 1; off < TPC; off <<= 1) cq += __shfl_xor(cq, off);
+  const uint32_t cq_hi = __shfl_down(cq, TPC);  // the next coarse bin's count
+  MselHead* hd = P.head + sl;
+  if ((tid & (2 * TPC - 1)) == 0) hd->coarse[tid / (2 * TPC)] = cq | (cq_hi << 16);
+  __syncthreads();
+  // counting sort of the slice's keys by bin (order inside a bin is free)
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    if (bin[j] != 0xffffffffu) {
+      const uint32_t slot = atomicAdd(&hist[bin[j]], 1u);
+      srt[slot] = low[j] | ((uint32_t)(p0 + 64 * j - s0) << kMsShift);
+    }
+  }
+  __syncthreads();
+  uint32_t* so = P.sorted + sl * kMsSlice;
+  const int e = s0 + kMsSlice < N ? s0 + kMsSlice : N;
+  const int lo = s0 > A ? s0 : A, hi = e < Cc ? e : Cc;
+  const int nc = hi > lo ? hi - lo : 0;
+  for (int i = tid; i < nc; i += kMsThreads) so[i] = srt[i];
+  if (tid == 0) {
+    hd->ncand = (uint32_t)nc;
+    hd->kc = kc;
+  }
+}
+
+// Bin (from the top) of a 64-bin histogram, one bin per lane of the calling
+// wave, where the count from the top first reaches `need`, and the count
+// strictly above it.  Wave-uniform results.
+__device__ __forceinline__ void find64(uint32_t c, uint32_t need, int lane, uint32_t& d,
+                                       uint32_t& above) {
+  uint32_t inc = c;  // inclusive suffix: bins >= lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(inc, off);
+    if (lane + off < 64) inc += y;
+  }
+  const uint32_t ab = inc - c;
+  const bool hit = ab < need && inc >= need;
+  const unsigned long long m = __ballot(hit);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;
+  d = (uint32_t)src;
+  above = __shfl(ab, src);
+}
+
+template <int kMsThreads>
+__global__ __launch_bounds__(kMsThreads) void msel_pick(const float* __restrict__ z, MselArgs a,
+                                                        const char* __restrict__ ws,
+                                                        int32_t* __restrict__ idx) {
+  constexpr int kMsWaves = kMsThreads / 64;
+  constexpr int kMsRows = kMsSlice / kMsThreads;  // rows of 64 positions per wave
+  // per-slice arrays, sized by the launch for its longest sequence
+  extern __shared__ uint32_t slice_lds[];
+  uint32_t* lst = slice_lds;
+  uint32_t* lcnt = lst + a.max_nsl;
+  uint32_t* abv = lcnt + a.max_nsl;
+  uint32_t* loff = abv + a.max_nsl;
+  __shared__ uint32_t lkey[kMsListCap];
+  __shared__ uint16_t lw[kMsListCap];
+  __shared__ uint32_t h2[kMsThreads];  // partial counts, then radix digits
+  __shared__ uint32_t wsum[2][kMsWaves];
+  __shared__ uint32_t sres[4];
+  const MselPtrs P = msel_ptrs((char*)ws, a.g);
+  const int lh = blockIdx.y, x = blockIdx.x;
+  const int b = seq_of_tile(a.st, x);
+  const int N = (int)a.st.N[b];
+  const int kept = (int)a.st.kept[b];
+  const int x0 = a.st.tile_off[b];
+  const int nsl = a.st.tile_off[b + 1] - x0;
+  const int me = x - x0;
+  const int s0 = me * kMsSlice;
+  int A, Cc;
+  prot_bounds(N, a.n_sink, a.n_recent, A, Cc);
+  const int ncand_u = Cc - A;
+  const uint32_t need = (uint32_t)(kept - (N - ncand_u));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float* zb = z + (int64_t)lh * a.T + a.st.cu[b];
+  const MselHead* heads = P.head + (int64_t)lh * a.nslice + x0;
+  const uint32_t* pres = P.pre + ((int64_t)lh * a.nslice + x0) * (kMsBins / 2);
+  const uint32_t* srts = P.sorted + ((int64_t)lh * a.nslice + x0) * kMsSlice;
+  // this slice's scores, loaded first (used only when writing, so the loads
+  // overlap the threshold search)
+  const int p0 = s0 + wave * (64 * kMsRows) + lane;
+  float zv[kMsRows];
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    const int p = p0 + 64 * j;
+    zv[j] = (p >= A && p < Cc) ? zb[p] : 0.f;
+  }
+  // protected positions before this slice: sinks below s0 and recents below s0
+  const uint32_t prot_before = (uint32_t)((s0 < A ? s0 : A) + (s0 > Cc ? s0 - Cc : 0));
+  uint32_t thr = kNoneKept, rem = 0u, Dbefore = prot_before, Tbefore = 0u;
+  if (need > 0u) {
+    const int kc = heads[0].kc;
+    // 1. coarse bin: counts of every slice added up; thread t sums coarse
+    // bin t % 64 over the slices w = t / 64 (mod the wave count), no atomics
+    const int bj = tid & 63, grp = tid >> 6;
+    uint32_t cacc = 0u;
+#pragma unroll 4
+    for (int w = grp; w < nsl; w += kMsWaves) {
+      const uint32_t w2 = heads[w].coarse[bj >> 1];
+      cacc += (bj & 1) ? (w2 >> 16) : (w2 & 0xffffu);
+    }
+    h2[tid] = cacc;
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t dc, ab;
+      uint32_t csum = 0u;
+      for (int g2 = 0; g2 < kMsWaves; ++g2) csum += h2[64 * g2 + lane];
+      find64(csum, need, lane, dc, ab);
+      if (lane == 0) {
+        sres[0] = dc;
+        sres[1] = ab;
+      }
+    }
+    __syncthreads();
+    const uint32_t dc = sres[0];
+    uint32_t need1 = need - sres[1];
+    // 2. the bin inside it, from every slice's bin starts, the same way
+    const int fb = (int)dc * 64 + bj;
+    uint32_t facc = 0u;
+#pragma unroll 4
+    for (int w = grp; w < nsl; w += kMsWaves) {
+      const uint32_t* pw = pres + (int64_t)w * (kMsBins / 2);
+      const uint32_t s_e = ld16(pw, fb);
+      const uint32_t s_n = fb + 1 < kMsBins ? ld16(pw, fb + 1) : heads[w].ncand;
+      facc += s_n - s_e;
+    }
+    __syncthreads();  // the coarse sums are read
+    h2[tid] = facc;
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t df, ab;
+      uint32_t csum = 0u;
+      for (int g2 = 0; g2 < kMsWaves; ++g2) csum += h2[64 * g2 + lane];
+      find64(csum, need1, lane, df, ab);
+      if (lane == 0) {
+        sres[0] = dc * 64 + df;
+        sres[1] = ab;
+      }
+    }
+    __syncthreads();
+    const uint32_t d1 = sres[0];
+    need1 -= sres[1];
+    // 3. every slice's run of bin d1 in its sorted keys, and its keys above it
+    for (int w = tid; w < nsl; w += kMsThreads) {
+      const uint32_t* pw = pres + (int64_t)w * (kMsBins / 2);
+      const uint32_t nc = heads[w].ncand;
+      const uint32_t st0 = ld16(pw, (int)d1);
+      const uint32_t en = d1 + 1 < (uint32_t)kMsBins ? ld16(pw, (int)d1 + 1) : nc;
+      lst[w] = st0;
+      lcnt[w] = en - st0;
+      abv[w] = nc - en;
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix of the runs over the slices
+      uint32_t run = 0u;
+      for (int base = 0; base < nsl; base += 64) {
+        const int w = base + lane;
+        const uint32_t c = w < nsl ? lcnt[w] : 0u;
+        uint32_t inc = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t y = __shfl_up(inc, off);
+          if (lane >= off) inc += y;
+        }
+        if (w < nsl) loff[w] = run + inc - c;
+        run += __shfl(inc, 63);
+      }
+      if (lane == 0) loff[nsl] = run;
+    }
+    __syncthreads();
+    const uint32_t nlist = loff[nsl];
+    const bool edge_bin = d1 == 0u || d1 == (uint32_t)(kMsBins - 1);  // keys beyond the window
+    const bool in_lds = nlist <= (uint32_t)kMsListCap;
+    // entry i of the bin's list: its key (the low kMsShift bits, or the whole
+    // key in an outermost bin) and its slice
+    auto entry = [&](uint32_t i, uint32_t& k, int& w) {
+      if (in_lds) {
+        k = lkey[i];
+        w = lw[i];
+        return;
+      }
+      int lo = 0, hi = nsl - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (loff[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      w = lo;
+      const uint32_t e = srts[(int64_t)w * kMsSlice + lst[w] + (i - loff[w])];
+      k = edge_bin ? order_key_bits(__float_as_uint(zb[w * kMsSlice + (int)(e >> kMsShift)]))
+                   : (e & ((1u << kMsShift) - 1u));
+    };
+    if (in_lds) {
+      for (uint32_t i = tid; i < nlist; i += kMsThreads) {
+        int lo = 0, hi = nsl - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (loff[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        const uint32_t e = srts[(int64_t)lo * kMsSlice + lst[lo] + (i - loff[lo])];
+        lkey[i] = edge_bin ? order_key_bits(__float_as_uint(zb[lo * kMsSlice + (int)(e >> kMsShift)]))
+                           : (e & ((1u << kMsShift) - 1u));
+        lw[i] = (uint16_t)lo;
+      }
+      __syncthreads();
+    }
+    // 4. exact threshold in the bin: 8-bit radix passes from the top bit
+    const int kbits = edge_bin ? 32 : kMsShift;
+    uint32_t pfx = 0u;
+    int done = 0;
+    while (done < kbits) {
+      const int nb = kbits - done < 8 ? kbits - done : 8;
+      const int sh = kbits - done - nb;
+      h2[tid] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < nlist; i += kMsThreads) {
+        uint32_t k;
+        int w;
+        entry(i, k, w);
+        if (done == 0 || (k >> (sh + nb)) == pfx) atomicAdd(&h2[(k >> sh) & ((1u << nb) - 1u)], 1u);
+      }
+      __syncthreads();
+      // digit from the top: thread t holds digit t
+      const uint32_t c = h2[tid];
+      uint32_t inc = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(inc, off);
+        if (lane + off < 64) inc += y;
+      }
+      if (lane == 0) wsum[0][wave] = inc;
+      __syncthreads();
+      uint32_t ab = inc - c;
+      for (int w2 = wave + 1; w2 < kMsWaves; ++w2) ab += wsum[0][w2];
+      if (ab < need1 && ab + c >= need1) {
+        sres[2] = (uint32_t)tid;
+        sres[3] = ab;
+      }
+      __syncthreads();
+      pfx = (pfx << nb) | sres[2];
+      need1 -= sres[3];
+      done += nb;
+      __syncthreads();
+    }
+    rem = need1;
+    // 5. the bin's keys above / equal to the threshold in the slices before
+    // this one, and the keys of those slices in bins above d1
+    uint32_t dl = 0u, tl = 0u;
+    for (uint32_t i = tid; i < nlist; i += kMsThreads) {
+      uint32_t k;
+      int w;
+      entry(i, k, w);
+      if (w < me) {
+        dl += k > pfx ? 1u : 0u;
+        tl += k == pfx ? 1u : 0u;
+      }
+    }
+    for (int w = tid; w < me; w += kMsThreads) dl += abv[w];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      dl += __shfl_xor(dl, off);
+      tl += __shfl_xor(tl, off);
+    }
+    if (lane == 0) {
+      wsum[0][wave] = dl;
+      wsum[1][wave] = tl;
+    }
+    __syncthreads();
+    dl = 0u;
+    tl = 0u;
+    for (int w2 = 0; w2 < kMsWaves; ++w2) {
+      dl += wsum[0][w2];
+      tl += wsum[1][w2];
+    }
+    Dbefore += dl;
+    Tbefore = tl;
+    const int kc_ = kc;
+    thr = edge_bin ? pfx : (((uint32_t)((int)d1 - kMsBins / 2 + kc_) << kMsShift) | pfx);
+  }
+  // 6. ordered writes of this slice (protected positions and padding carry
+  // keys above every score)
+  uint32_t key[kMsRows];
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    const int p = p0 + 64 * j;
+    key[j] = p >= N ? kPad
+                    : ((p < A || p >= Cc) ? kProt : order_key_bits(__float_as_uint(zv[j])));
+  }
+  uint32_t nd = 0u, nt = 0u;
+#pragma unroll
+  for (int j = 0; j < kMsRows; ++j) {
+    nd += (uint32_t)__popcll(__ballot(key[j] > thr && key[j] != kPad));
+    nt += (uint32_t)__popcll(__ballot(key[j] == thr));
+  }
+  if (lane == 0) {
+    wsum[0][wave] = nd;
+    wsum[1][wave] = nt;
+  }
+  __syncthreads();
+  uint32_t D = Dbefore, Tt = Tbefore;
+  for (int w = 0; w < wave; ++w) {
+    D += wsum[0][w];
+    Tt += wsum[1][w];
+  }
+  int32_t* out = idx + (int64_t)lh * a.Ktot + a.st.ko[b];
+  emit_round<kMsRows>(key, true, thr, rem, D, Tt, s0 + wave * (64 * kMsRows) + lane, kept, out);
+}
+
 }  // namespace
 
 hipError_t launch_head_stats(const float* s, const SeqTable& st, int L, int Hkv, double* part,
@@ -874,6 +1407,68 @@ hipError_t launch_select(const float* z, const SeqTable& st, int L, int Hkv, int
   }
   hipLaunchKernelGGL(select_kernel, dim3(st.B, L * Hkv), dim3(kSelThreads), 0, stream, z, st, T, K,
                      n_sink, n_recent, idx);
+  return hipGetLastError();
+}
+
+MselGeom msel_geometry(const SeqTable& st, int L, int Hkv) {
+  MselGeom g{};
+  const size_t LH = (size_t)L * Hkv;
+  const size_t ns = (size_t)st.tile_off[st.B];
+  g.d.off_head = 0;
+  g.d.off_pre = align256r(LH * ns * sizeof(MselHead));
+  g.d.off_sorted = g.d.off_pre + align256r(LH * ns * (kMsBins / 2) * sizeof(uint32_t));
+  g.bytes = g.d.off_sorted + align256r(LH * ns * kMsSlice * sizeof(uint32_t));
+  return g;
+}
+
+hipError_t launch_msel(const float* src, bool refine, float* z, const SeqTable& st, int L,
+                       int Hkv, int n_sink, int n_recent, const RefineParams& rp, int32_t* idx,
+                       char* ws, const MselGeom& geo, hipStream_t stream) {
+  MselArgs a{};
+  a.st = st;
+  a.Hkv = Hkv;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.nslice = st.tile_off[st.B];
+  a.max_nsl = 1;
+  for (int b = 0; b < st.B; ++b) {
+    const int n = st.tile_off[b + 1] - st.tile_off[b];
+    a.max_nsl = n > a.max_nsl ? n : a.max_nsl;
+  }
+  a.T = 0;
+  a.Ktot = 0;
+  for (int b = 0; b < st.B; ++b) {
+    a.T += st.N[b];
+    a.Ktot += st.kept[b];
+  }
+  a.g = geo.d;
+  a.half = rp.pool / 2;
+  a.gamma = rp.gamma;
+  a.r2 = rp.r2;
+  a.beta_lo = rp.beta_lo;
+  a.beta_hi = rp.beta_hi;
+  a.beta_in = rp.beta_in;
+  a.stats = rp.stats;
+  a.beta_out = rp.beta_out;
+  const dim3 grid(a.nslice, L * Hkv);
+  const bool big = (int64_t)a.nslice * L * Hkv >= kMsBigGrid;
+  const dim3 block(big ? 256 : 1024);
+  if (refine && big)
+    hipLaunchKernelGGL((msel_bin<true, 256>), grid, block, 0, stream, src, z, a, ws);
+  else if (refine)
+    hipLaunchKernelGGL((msel_bin<true, 1024>), grid, block, 0, stream, src, z, a, ws);
+  else if (big)
+    hipLaunchKernelGGL((msel_bin<false, 256>), grid, block, 0, stream, src, z, a, ws);
+  else
+    hipLaunchKernelGGL((msel_bin<false, 1024>), grid, block, 0, stream, src, z, a, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)(4 * a.max_nsl + 1) * sizeof(uint32_t);
+  const float* zz = refine ? (const float*)z : src;
+  if (big)
+    hipLaunchKernelGGL((msel_pick<256>), grid, block, lds, stream, zz, a, (const char*)ws, idx);
+  else
+    hipLaunchKernelGGL((msel_pick<1024>), grid, block, lds, stream, zz, a, (const char*)ws, idx);
   return hipGetLastError();
 }
 
