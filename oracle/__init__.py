@@ -37,6 +37,24 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+_CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build_sanitized() -> str:
+    """The oracle built by clang with AddressSanitizer and
+    UndefinedBehaviorSanitizer (no OpenMP, so one thread; FP contraction still
+    off), for the test suite's memory-safety run of the host code.  The
+    sanitizer runtime must be preloaded into the process that loads it."""
+    tmp = _SAN_LIB + ".tmp"
+    subprocess.check_call([_CLANG, "-O1", "-g", "-fno-omit-frame-pointer",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-ffp-contract=off", "-std=c99", "-fPIC", "-shared", _SRC, "-o", tmp,
+                           "-lm"])
+    os.replace(tmp, _SAN_LIB)
+    return _SAN_LIB
+
+
 _lib = None
 
 

@@ -34,7 +34,9 @@ import re
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhubkv.so")
+# HUBKV_LIB names another build of the library (the test suite's sanitized
+# host build); by default the in-tree libhubkv.so
+LIB_PATH = os.environ.get("HUBKV_LIB") or os.path.join(HERE, "libhubkv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "hubkv.h")
 
 HUBKV_F32, HUBKV_BF16 = 0, 1

@@ -53,5 +53,36 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+SAN_OUT = os.path.join(BUILD_DIR, "libhubkv_san.so")
+# host-side sanitizers only: every -fsanitize applies to the host pass
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_sanitized() -> str:
+    """libhubkv_san.so: the C ABI layer (abi.cpp: validation, workspace sizing,
+    dispatch) compiled with AddressSanitizer and UndefinedBehaviorSanitizer on
+    its host code, linked with the kernels of the regular build.  For the test
+    suite's host-side memory-safety run; the GPU code is not instrumented."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(x)[0] + ".o") for x in SOURCES if x != "abi.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    obj = os.path.join(BUILD_DIR, "abi_san.o")
+    flags = [f for f in FLAGS if f != "-O3"]
+    cmd = [HIPCC, "-x", "hip", *flags, *SAN_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on abi.cpp (sanitized):\n" + r.stderr)
+    tmp = SAN_OUT + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed (sanitized):\n" + r.stderr)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
