@@ -36,16 +36,16 @@ COPY_BYTES = 1 << 30         # size of one calibration copy
 # WRITE_SIZE) of `bench.py --steps 5 --warmup 1 --no-cpu-baseline`, each scaled
 # by the same counter over a plain 1 GiB device copy (`bench.py
 # --copy-calibration`).  Valid only for the score source they were taken on.
-SCORE_TRAFFIC = {"sha256": "8c1eca34354a8732b72584a8fec191ad327bb4c7ce077b92855dc8d6646ac2a6", "workload": 2,
-                 "fetch_bytes": 546608317, "write_bytes": 4350993}
+SCORE_TRAFFIC = {"sha256": "8e4c6ddedc997dfcedafdd1267de45c1e2c7b1c853c64f8410c1731b14945500", "workload": 2,
+                 "fetch_bytes": 546619531, "write_bytes": 4350961}
 
 
 # The same for one full-cache h2o_step launch of the decode workload (scores
 # only, fixed slots), from `bench.py --workload 4 --steps 8 --warmup 1
 # --no-cpu-baseline` (the last 1000 launches).  Valid only for the decode
 # source it was taken on.
-DECODE_TRAFFIC = {"sha256": "af5eb02272d454f36ae5a41f5beed47461383c1c1d7d1bc0f043c28f94020c45", "workload": 4,
-                  "fetch_bytes": 554208249, "write_bytes": 8683520}
+DECODE_TRAFFIC = {"sha256": "4a80c48438d934ac10cce5aa02e8e9948d4c08f45a07775ef409e80d9bd564d2", "workload": 4,
+                  "fetch_bytes": 554208196, "write_bytes": 8683520}
 
 
 def _source_sha(files) -> str:
