@@ -44,8 +44,8 @@ SCORE_TRAFFIC = {"sha256": "8e4c6ddedc997dfcedafdd1267de45c1e2c7b1c853c64f8410c1
 # only, fixed slots), from `bench.py --workload 4 --steps 8 --warmup 1
 # --no-cpu-baseline` (the last 1000 launches).  Valid only for the decode
 # source it was taken on.
-DECODE_TRAFFIC = {"sha256": "4a80c48438d934ac10cce5aa02e8e9948d4c08f45a07775ef409e80d9bd564d2", "workload": 4,
-                  "fetch_bytes": 554208196, "write_bytes": 8683520}
+DECODE_TRAFFIC = {"sha256": "4e7bdaaa08e2b69f627ab86ee505c73bda715903e91d123f56394fde65ccbd2b", "workload": 4,
+                  "fetch_bytes": 554376088, "write_bytes": 8683520}
 
 
 def _source_sha(files) -> str:
@@ -655,7 +655,7 @@ def main(argv=None):
     kernels = {"score": "score_pass_mfma<1> (row partials) + score_pass_mfma<2> (fold, column sums)" if elem == 2 else
                "score_stats_f32 + score_combine + score_probs_f32 + stats_final",
                "refine": "refine_kernel",
-               "refine_select": "msel_prep<refine> + msel_hist + msel_emit",
+               "refine_select": "msel_bin<refine> + msel_pick",
                "select": ("lsel_init + lsel_floor_level<0..2> + lsel_pool_level<0..2> + lsel_count"
                           " + lsel_emit_count + lsel_emit") if args.layer_budget else "select_kernel",
                "compact": "compact_layer_kernel" if args.layer_budget else "compact_kernel"}

@@ -119,6 +119,22 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     om[h] = -INFINITY;
     os[h] = 0.f;
   }
+  // this lane's piece of every query head, in registers for the whole sweep
+  float qv[KG][EPL];
+#pragma unroll
+  for (int h = 0; h < KG; ++h)
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) qv[h][x] = h < G ? qs[h][piece * EPL + x] : 0.f;
+  // the accumulated scores this thread updates after the sweep, loaded now so
+  // that the update does not wait on memory (the host limits C to 8192)
+  constexpr int kAccPer = 16;
+  static_assert(kAccPer * kH2OThreads >= 8192, "every slot of the largest cache has a register");
+  float accv[kAccPer];
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) {
+    const int j = tid + i * kH2OThreads;
+    accv[i] = j < C ? A[j] : 0.f;
+  }
   // positions of the slots, staged in LDS with coalesced loads
   for (int j = tid; j < C; j += kH2OThreads) pl[j] = P[j];
   // row groups are software-pipelined: the next kUnroll groups' loads are in
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
         if (h < G) {  // G is uniform: every lane takes the same branch
           float d = 0.f;
 #pragma unroll
-          for (int x = 0; x < EPL; ++x) d = fmaf(qs[h][piece * EPL + x], kv[x], d);
+          for (int x = 0; x < EPL; ++x) d = fmaf(qv[h][x], kv[x], d);
 #pragma unroll
           for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
           const float x2 = occ ? d * c2 : -INFINITY;
@@ -247,7 +263,10 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   const int rslot = a.ring ? nheavy + (int)(t % a.n_recent) : -1;  // the new token's ring slot
   unsigned long long best = ~0ull;
   int best_slot = -1, first_empty = 0x7fffffff;
-  for (int j = tid; j < C; j += kH2OThreads) {
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) {
+    const int j = tid + i * kH2OThreads;
+    if (j >= C) break;
     const int32_t pj = pl[j];
     float add = 0.f;
     for (int h = 0; h < G; ++h) {
@@ -259,7 +278,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     if (pj < 0) {
       if (j < nheavy) first_empty = min(first_empty, j);
     } else {
-      const float na = A[j] + add;
+      const float na = accv[i] + add;
       A[j] = na;
       if (j == rslot) ring_acc = na;
       if (pj >= lo && pj <= hi) {
