@@ -44,7 +44,7 @@ SCORE_TRAFFIC = {"sha256": "8e4c6ddedc997dfcedafdd1267de45c1e2c7b1c853c64f8410c1
 # only, fixed slots), from `bench.py --workload 4 --steps 8 --warmup 1
 # --no-cpu-baseline` (the last 1000 launches).  Valid only for the decode
 # source it was taken on.
-DECODE_TRAFFIC = {"sha256": "4e7bdaaa08e2b69f627ab86ee505c73bda715903e91d123f56394fde65ccbd2b", "workload": 4,
+DECODE_TRAFFIC = {"sha256": "2b6e1df04948ba04b0d116f5af1c2aafd0eba998d01c655fd5a4317e71bb6192", "workload": 4,
                   "fetch_bytes": 554376088, "write_bytes": 8683520}
 
 

@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (src[u] >= 0) {
-        kv[u] = kin[src[u] * cs.ki.s_t];
-        vv[u] = vin[src[u] * cs.vi.s_t];
+        kv[u] = __builtin_nontemporal_load(&kin[src[u] * cs.ki.s_t]);
+        vv[u] = __builtin_nontemporal_load(&vin[src[u] * cs.vi.s_t]);
       }
     }
 #pragma unroll

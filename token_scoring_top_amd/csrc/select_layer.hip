@@ -677,8 +677,8 @@ __global__ __launch_bounds__(kT) void compact_layer_kernel(
 #pragma unroll
     for (int q = 0; q < kCrows; ++q)
       if (src[q] >= 0) {
-        kv[q] = kin[src[q]];
-        vv[q] = vin[src[q]];
+        kv[q] = __builtin_nontemporal_load(&kin[src[q]]);
+        vv[q] = __builtin_nontemporal_load(&vin[src[q]]);
       }
 #pragma unroll
     for (int q = 0; q < kCrows; ++q)
