@@ -145,6 +145,13 @@ def test_select_validation():
     assert call([30, 30], ws=P + 8) == EALIGN
     nb = L.hubkv_select_workspace(2, sl, 1, 2)
     assert nb > 0 and call([30, 30], wsb=nb - 1) == EWS
+    # per slice: a 256-byte head record, 4096 16-bit bin starts, 4096 sorted keys
+    per_slice = 256 + 4096 * 2 + 4096 * 4
+    four = a64([3000, 5000, 131, 20000])   # 1 + 2 + 1 + 5 slices
+    assert L.hubkv_select_workspace(4, four, 7, 9) == 7 * 9 * 9 * per_slice
+    # 256 (layer, head, sequence) units fill the chip: one work-group per
+    # unit, no slices, and the workspace shrinks to one aligned block
+    assert L.hubkv_select_workspace(4, four, 8, 8) == 256
 
 
 def test_refine_select_validation():

@@ -176,6 +176,10 @@ SELECT_CASES = [
     # over 1024 slices of 4096 positions in one call: the 256-thread work-groups
     ([400000, 300000, 200001, 150000], 2, 2, 0.1, 4, 64, "special"),
     ([400000, 300000, 200001, 150000], 2, 2, 0.1, 4, 64, "ties"),
+    # 256 (layer, head, sequence) units fill the chip: the one-work-group
+    # select; 252 units: the sliced one
+    ([3000, 5000, 131, 20000], 8, 8, 0.1, 4, 64, "special"),
+    ([3000, 5000, 131, 20000], 7, 9, 0.1, 4, 64, "ties"),
 ]
 
 
@@ -243,6 +247,7 @@ RSEL_CASES = [
     ([32768], 1, 8, "attention", False, 5, 0.5, 0.1, 0.1, 4, 64),
     ([131072, 5], 1, 2, "attention", False, 5, 0.5, 0.1, 0.1, 4, 64),       # a 5-token sequence
     ([200000, 99999, 3], 2, 8, "attention", True, 5, 0.5, 0.1, 0.1, 4, 64),  # 1200 slices
+    ([3000, 5000, 131, 20000], 8, 8, "attention", True, 5, 0.5, 0.1, 0.1, 4, 64),  # 256 units
 ]
 
 
