@@ -311,22 +311,24 @@ def test_attention_output_free_running_stream(dtype, include_self):
     assert diverged.mean() <= 0.5
 
 
-def test_free_running_decode_workload():
+@pytest.mark.parametrize("ring", [False, True], ids=["fixed", "ring"])
+def test_free_running_decode_workload(ring):
     """The decode workload at full size (16 sequences x 32 KV heads, 2048 heavy
-    + 2048 recent slots, d 128, bf16) streamed through h2o_step from an empty
-    cache: the 16384-token prompt, then the 512 decode steps.  The oracle
-    follows 16 sampled (sequence, KV head) units beside the GPU, each side on
-    its own state, fed the same per-step inputs.  Every first divergence of a
-    unit must be a near-tie of the oracle's eviction candidates (their two
-    smallest accumulated scores within the bf16 bar); a unit that never
-    diverges must end with the same tokens in the same slots and the same
-    accumulated scores within that bar."""
+    + 2048 recent slots, d 128, bf16) streamed through h2o_step (or
+    h2o_step_ring) from an empty cache: the 16384-token prompt, then the 512
+    decode steps.  The oracle follows 16 sampled (sequence, KV head) units
+    beside the GPU, each side on its own state, fed the same per-step inputs.
+    Every first divergence of a unit must be a near-tie of the oracle's
+    eviction candidates (their two smallest accumulated scores within the
+    bf16 bar); a unit that never diverges must end with the same tokens (in
+    the same slots with fixed slots; matched by position with the ring, whose
+    slots differ) and the same accumulated scores within that bar."""
     import bench
     w = S.workload(4)
     total = w.prompt + w.decode
-    note(f"  streaming {total} steps on the GPU, the oracle beside it on "
-         f"{len(bench.DECODE_SAMPLE_UNITS)} units")
-    ds = bench.DecodeStream(w, total)
+    note(f"  streaming {total} steps ({'ring' if ring else 'fixed'} slots) on the GPU, the "
+         f"oracle beside it on {len(bench.DECODE_SAMPLE_UNITS)} units")
+    ds = bench.DecodeStream(w, total, ring=ring)
     ds.run_gpu(total, oracle_beside=True)
     ds.run_oracle(total)
     st = ds.stats()
@@ -348,7 +350,13 @@ def test_free_running_decode_workload():
     for u in range(len(ds.units)):
         if u in diverged:
             continue
-        np.testing.assert_array_equal(pos_g[u], ds.ost["pos"][u, 0])
-        assert rel_err(acc_g[u], ds.ost["acc"][u, 0], 1e-30).max() < 2e-2
+        po, ao = ds.ost["pos"][u, 0], ds.ost["acc"][u, 0]
+        if ring:
+            og, oo = np.argsort(pos_g[u]), np.argsort(po)
+            np.testing.assert_array_equal(pos_g[u][og], po[oo])
+            assert rel_err(acc_g[u][og], ao[oo], 1e-30).max() < 2e-2
+        else:
+            np.testing.assert_array_equal(pos_g[u], po)
+            assert rel_err(acc_g[u], ao, 1e-30).max() < 2e-2
     if not diverged:
         assert st["final_set_overlap_min"] == 1.0
