@@ -15,15 +15,19 @@
  *   hubkv_nestedkv a second base score from the keys alone (NestedKV)
  *   h2o_step       one streaming (decode) step of H2O greedy eviction
  *   h2o_step_ring  the same step with the recent window kept in a ring of slots
+ *   hubkv_score_noalloc
+ *                  hubkv_score on a fixed library-held scratch array, for
+ *                  callers that cannot allocate
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE memory unless the parameter says "host".
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream) and never synchronises it.
- *   - The library never allocates device memory and keeps no mutable global
- *     state.  Scratch space is a caller-provided workspace whose size comes
- *     from the matching *_workspace() query; it must stay alive until the
- *     enqueued work has finished.
+ *   - The library never allocates device memory.  Scratch space is a
+ *     caller-provided workspace whose size comes from the matching
+ *     *_workspace() query; it must stay alive until the enqueued work has
+ *     finished.  The one exception is hubkv_score_noalloc's fixed per-device
+ *     scratch array, the library's only mutable global state.
  *   - Host arrays (sequence lengths, kept counts, positions) are read during
  *     the call only.
  *   - Arguments are validated on the host before anything is enqueued.  On a

@@ -13,10 +13,16 @@
 // sequence) keep the protected positions and the largest remaining z, ties to
 // the lower position, written ascending.
 //
-// Selection is an exact radix select on order-preserving 32-bit keys of z
-// (histogram passes in LDS, the first one over the keys' own range), followed
-// by one ordered emission pass that ranks kept positions with ballots.  The
-// result is deterministic and independent of thread timing.
+// Selection is exact and integer throughout, on order-preserving 32-bit keys
+// of z, with one ordered emission pass that ranks kept positions with
+// ballots.  Two implementations give the same result bit for bit:
+//   - many work-groups per head (msel_bin + msel_pick, below): 4096-position
+//     slices binned around a sampled estimate of the threshold, every slice
+//     resolving the threshold itself from all slices' bin data;
+//   - one work-group per head (select_kernel): radix histogram passes in
+//     LDS, the first over the keys' own range, for calls whose units fill the
+//     chip alone and for sequences beyond the slices' reach.
+// The result is deterministic and independent of thread timing.
 #include "internal.hpp"
 
 namespace hubkv {
