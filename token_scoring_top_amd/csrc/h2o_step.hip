@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   int32_t* pl = (int32_t*)(lg + G_of(a) * a.C);
   float* part = (float*)(pl + a.C);
   __shared__ float qs[KG][D];
+  __shared__ u32x4 newrow[2][LPR];  // the new token's K and V rows, 16 bytes a lane
   __shared__ float red[WAVES][KG], red2[WAVES][KG];
   __shared__ float Mh[KG], iLh[KG], selfx[KG], pself[KG];
   __shared__ unsigned long long cand_key[WAVES];
@@ -104,39 +105,14 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float c2 = a.scale * kLog2eH;
 
-  for (int i = tid; i < G * D; i += kH2OThreads)
-    qs[i / D][i % D] = to_f<T>(q[((int64_t)b * a.Hq + g * G + i / D) * D + i % D]);
-  __syncthreads();
-
-  // ---- logits over the occupied slots
+  // ---- logits over the occupied slots.  Every load that depends on nothing
+  // computed here goes out first, before the first wait: the first K row
+  // groups, this thread's accumulated scores, the slot positions, the new
+  // K/V rows written at the end, and the query.
   const T* Kc = k_cache + (int64_t)u * C * D;
   const int32_t* P = pos + (int64_t)u * C;
   float* A = acc + (int64_t)u * C;
   const int piece = lane % LPR, rsub = lane / LPR;
-  float om[KG], os[KG];
-#pragma unroll
-  for (int h = 0; h < KG; ++h) {
-    om[h] = -INFINITY;
-    os[h] = 0.f;
-  }
-  // this lane's piece of every query head, in registers for the whole sweep
-  float qv[KG][EPL];
-#pragma unroll
-  for (int h = 0; h < KG; ++h)
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) qv[h][x] = h < G ? qs[h][piece * EPL + x] : 0.f;
-  // the accumulated scores this thread updates after the sweep, loaded now so
-  // that the update does not wait on memory (the host limits C to 8192)
-  constexpr int kAccPer = 16;
-  static_assert(kAccPer * kH2OThreads >= 8192, "every slot of the largest cache has a register");
-  float accv[kAccPer];
-#pragma unroll
-  for (int i = 0; i < kAccPer; ++i) {
-    const int j = tid + i * kH2OThreads;
-    accv[i] = j < C ? A[j] : 0.f;
-  }
-  // positions of the slots, staged in LDS with coalesced loads
-  for (int j = tid; j < C; j += kH2OThreads) pl[j] = P[j];
   // row groups are software-pipelined: the next kUnroll groups' loads are in
   // flight while the current kUnroll groups are reduced
   constexpr int kUnroll = 4;
@@ -153,7 +129,39 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
     }
   };
   load_group(wave * RPW, nxt);
-  __syncthreads();  // positions staged
+  // the accumulated scores this thread updates after the sweep, in registers
+  // (the host limits C to 8192)
+  constexpr int kAccPer = 16;
+  static_assert(kAccPer * kH2OThreads >= 8192, "every slot of the largest cache has a register");
+  float accv[kAccPer];
+#pragma unroll
+  for (int i = 0; i < kAccPer; ++i) {
+    const int j = tid + i * kH2OThreads;
+    accv[i] = j < C ? A[j] : 0.f;
+  }
+  // positions of the slots, the new token's K and V rows and the query,
+  // staged in LDS with coalesced loads
+  if (wave == 0 && lane < LPR) {
+    const int64_t src = ((int64_t)b * a.Hkv + g) * D + lane * EPL;
+    newrow[0][lane] = *(const u32x4*)(k_new + src);
+    newrow[1][lane] = *(const u32x4*)(v_new + src);
+  }
+  for (int j = tid; j < C; j += kH2OThreads) pl[j] = P[j];
+  for (int i = tid; i < G * D; i += kH2OThreads)
+    qs[i / D][i % D] = to_f<T>(q[((int64_t)b * a.Hq + g * G + i / D) * D + i % D]);
+  __syncthreads();  // positions and query staged
+  float om[KG], os[KG];
+#pragma unroll
+  for (int h = 0; h < KG; ++h) {
+    om[h] = -INFINITY;
+    os[h] = 0.f;
+  }
+  // this lane's piece of every query head, in registers for the whole sweep
+  float qv[KG][EPL];
+#pragma unroll
+  for (int h = 0; h < KG; ++h)
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) qv[h][x] = h < G ? qs[h][piece * EPL + x] : 0.f;
   for (int j0 = wave * RPW; j0 < C; j0 += kStep) {
     u32x4 raw[kUnroll];
 #pragma unroll
@@ -437,7 +445,6 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
       pos[(int64_t)u * C + slot] = (int32_t)t;
     }
     if (wave == 0 && lane < LPR) {
-      const int64_t src = ((int64_t)b * a.Hkv + g) * D + lane * EPL;
       const int64_t dst = ((int64_t)u * C + slot) * D + lane * EPL;
       if (mv >= 0) {
         // the leaving token's row goes to its heavy slot before the new row
@@ -448,8 +455,8 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
         *(u32x4*)(k_cache + mdst) = kr;
         *(u32x4*)(v_cache + mdst) = vr;
       }
-      *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_new + src);
-      *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_new + src);
+      *(u32x4*)(k_cache + dst) = newrow[0][lane];
+      *(u32x4*)(v_cache + dst) = newrow[1][lane];
     }
   }
 }
