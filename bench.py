@@ -44,8 +44,8 @@ SCORE_TRAFFIC = {"sha256": "8e4c6ddedc997dfcedafdd1267de45c1e2c7b1c853c64f8410c1
 # only, fixed slots), from `bench.py --workload 4 --steps 8 --warmup 1
 # --no-cpu-baseline` (the last 1000 launches).  Valid only for the decode
 # source it was taken on.
-DECODE_TRAFFIC = {"sha256": "d347c98998aec838184fe62dcbd0b5e33071282e5694a5e920f2ba9ba6440ec6", "workload": 4,
-                  "fetch_bytes": 554365689, "write_bytes": 8683520}
+DECODE_TRAFFIC = {"sha256": "73b295d5acfa5d786c8b46c62cbb7493d36e9df5701b0aac7745b0e402b0ec39", "workload": 4,
+                  "fetch_bytes": 554371979, "write_bytes": 8683520}
 
 
 def _source_sha(files) -> str:

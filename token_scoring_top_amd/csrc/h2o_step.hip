@@ -56,6 +56,25 @@ struct Words<1> {
   typedef uint32_t type;
 };
 
+// Sum over each group of N consecutive lanes (N = 8, 16 or 32; groups start
+// at multiples of N), left in every lane of the group.  DPP moves on the VALU
+// (quad permutes [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors)
+// instead of LDS-crossbar shuffles; a 32-lane group adds one shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float row_sum(float d) {
+  static_assert(N == 8 || N == 16 || N == 32, "groups of 8, 16 or 32 lanes");
+  d += dpp_mov<0xB1>(d);   // lane ^ 1
+  d += dpp_mov<0x4E>(d);   // lane ^ 2: every lane holds its quad's sum
+  d += dpp_mov<0x141>(d);  // half-row mirror: the other quad of its 8 lanes
+  if constexpr (N >= 16) d += dpp_mov<0x140>(d);  // row mirror: the other 8 of its 16
+  if constexpr (N == 32) d += __shfl_xor(d, 16);
+  return d;
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f(T x);
 template <>
@@ -150,12 +169,6 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   for (int i = tid; i < G * D; i += kH2OThreads)
     qs[i / D][i % D] = to_f<T>(q[((int64_t)b * a.Hq + g * G + i / D) * D + i % D]);
   __syncthreads();  // positions and query staged
-  float om[KG], os[KG];
-#pragma unroll
-  for (int h = 0; h < KG; ++h) {
-    om[h] = -INFINITY;
-    os[h] = 0.f;
-  }
   // this lane's piece of every query head, in registers for the whole sweep
   float qv[KG][EPL];
 #pragma unroll
@@ -181,19 +194,9 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
           float d = 0.f;
 #pragma unroll
           for (int x = 0; x < EPL; ++x) d = fmaf(qv[h][x], kv[x], d);
-#pragma unroll
-          for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+          d = row_sum<LPR>(d);
           const float x2 = occ ? d * c2 : -INFINITY;
-          if (piece == 0 && j < C) {
-            lg[h * C + j] = x2;
-            // running softmax statistics of this lane's slots
-            if (x2 > -INFINITY) {
-              const float mn = fmaxf(om[h], x2);
-              os[h] = os[h] * __builtin_amdgcn_exp2f(om[h] - mn) +
-                      __builtin_amdgcn_exp2f(x2 - mn);
-              om[h] = mn;
-            }
-          }
+          if (piece == 0 && j < C) lg[h * C + j] = x2;
         }
       }
     }
@@ -210,7 +213,26 @@ __global__ __launch_bounds__(kH2OThreads) void h2o_step_kernel(
   }
   __syncthreads();
 
-  // ---- softmax statistics per query head: merge the lanes' running (m, s)
+  // ---- each thread's share of the softmax statistics, from the logits in
+  // LDS (every lane busy, one exponential per logit): its slots' maximum,
+  // then their sum of exp2(x - maximum)
+  float om[KG], os[KG];
+#pragma unroll
+  for (int h = 0; h < KG; ++h) {
+    om[h] = -INFINITY;
+    os[h] = 0.f;
+    if (h < G) {  // G is uniform: every lane takes the same branch
+      float m = -INFINITY;
+      for (int j = tid; j < C; j += kH2OThreads) m = fmaxf(m, lg[h * C + j]);
+      float sm = 0.f;
+      if (m > -INFINITY)
+        for (int j = tid; j < C; j += kH2OThreads) sm += __builtin_amdgcn_exp2f(lg[h * C + j] - m);
+      om[h] = m;
+      os[h] = sm;
+    }
+  }
+
+  // ---- softmax statistics per query head: merge the threads' (m, s)
 #pragma unroll
   for (int h = 0; h < KG; ++h) {
     if (h < G) {  // G is uniform: every lane takes the same branch
