@@ -177,6 +177,23 @@ def test_refine_select_validation():
     assert call(wsb=nb - 1) == EWS
 
 
+def test_nothing_kept_writes_nothing():
+    # kept = 0 everywhere (no protected tokens): the calls validate their
+    # arguments, accept empty (null) row outputs, and return before any
+    # launch, so they run here without a GPU
+    L = hk.lib()
+    sl = a64([1, 700])
+    zero = a64([0, 0])
+    nb = L.hubkv_select_workspace(2, sl, 2, 3)
+    assert L.hubkv_select(P, 2, sl, 2, 3, zero, 0, 0, None, P, nb, None) == 0
+    assert L.hubkv_select(None, 2, sl, 2, 3, zero, 0, 0, None, P, nb, None) == EALIGN
+    assert L.hubkv_select(P, 2, sl, 2, 3, zero, 1, 0, None, P, nb, None) == EINVAL  # a sink must be kept
+    assert L.hubkv_compact(P, P, 1, None, 2, sl, zero, 2, 3, 128, None, None, None) == 0
+    assert L.hubkv_compact(P, P, 1, None, 2, sl, a64([0, 1]), 2, 3, 128, None, None, None) == EALIGN
+    lk = a64([0, 0])  # L = 1, B = 2
+    assert L.hubkv_compact_layer(P, P, 1, None, None, 2, sl, 1, 3, lk, 128, None, None, None) == 0
+
+
 def test_compact_validation():
     L = hk.lib()
     sl = a64([100])

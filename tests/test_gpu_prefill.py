@@ -314,6 +314,39 @@ def test_select_longest_sequences(n):
     np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
 
 
+def test_nothing_kept():
+    """kept = 0 in every sequence (no protected tokens): select, refine+select
+    and both compactions write no row and take empty outputs, refine+select
+    still writes z and beta, and the layer-wide select reports zero per head;
+    with one sequence keeping none beside others, bit-exact as usual."""
+    seqlens, L, Hkv = [1, 700], 2, 3
+    s = S.random_scores(seqlens, L, Hkv, seed=77)
+    st = torch.from_numpy(oracle.head_stats(s, seqlens)).cuda()
+    sd = to_dev(s, "f32")
+    zero = np.array([0, 0], np.int64)
+    z_g, b_g, idx_g = hk.hubkv_refine_select(sd, seqlens, zero, 0, 0, head_stats=st)
+    idx2 = hk.hubkv_select(z_g, seqlens, zero, 0, 0)
+    rng = np.random.default_rng(5)
+    K = S.round_bf16(rng.standard_normal((L, Hkv, sum(seqlens), 128)).astype(np.float32))
+    Kd = to_dev(K, "bf16")
+    ko, vo = hk.hubkv_compact(Kd, Kd, idx2, seqlens, zero)
+    lk = [[0, 0], [0, 0]]
+    il, hkl = hk.hubkv_select_layer(z_g, seqlens, lk, 0, 0, 0)
+    kl, vl = hk.hubkv_compact_layer(Kd, Kd, il, hkl, seqlens, lk)
+    torch.cuda.synchronize()
+    assert idx_g.numel() == idx2.numel() == ko.numel() == vo.numel() == 0
+    assert il.numel() == kl.numel() == vl.numel() == 0
+    np.testing.assert_array_equal(hkl.cpu().numpy(), 0)
+    b = b_g.cpu().numpy()
+    np.testing.assert_array_equal(z_g.cpu().numpy(), oracle.refine(s, seqlens, b, 5, 0.5, 0.1))
+    # one sequence keeps none, the other 70
+    kept = np.array([0, 70], np.int64)
+    z1, b1, i1 = hk.hubkv_refine_select(sd, seqlens, kept, 0, 0, head_stats=st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(i1.cpu().numpy(),
+                                  oracle.select(z1.cpu().numpy(), seqlens, kept, 0, 0))
+
+
 # ---------------------------------------------------------------- compact ---
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_compact_bitexact_given_indices(dtype, d):

@@ -243,7 +243,7 @@ def test_h2o_step(seed):
     C = heavy + recent
     fill = int(rng.choice([C, C, int(rng.integers(0, C + 1))]))
     t = fill + int(rng.integers(0, 1000))
-    n_sink = int(rng.choice([0, 2, 10]))
+    n_sink = min(int(rng.choice([0, 2, 10])), heavy)  # the windows fit the cache
     inc = int(rng.integers(0, 2))
     w = S.workload(4).with_(B=B, Hkv=Hkv, Hq=G * Hkv, d=d, heavy=heavy, recent=recent,
                             dtype=dtype, n_sink=n_sink)

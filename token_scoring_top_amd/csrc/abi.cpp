@@ -69,6 +69,14 @@ int check_kept(SeqTable& st, const int64_t* kept, int n_sink, int n_recent, bool
   return HUBKV_OK;
 }
 
+// Rows kept over all sequences (after check_kept).  A call that keeps none
+// writes no row, so its row outputs may be null.
+int64_t kept_total(const SeqTable& st) {
+  int64_t K = 0;
+  for (int b = 0; b < st.B; ++b) K += st.kept[b];
+  return K;
+}
+
 int check_dtype_d(int dtype, int d) {
   if (dtype != HUBKV_F32 && dtype != HUBKV_BF16) return HUBKV_EDTYPE;
   if (d != 64 && d != 128) return HUBKV_EDTYPE;
@@ -456,7 +464,9 @@ int hubkv_select(const float* z, int B, const int64_t* seqlens, int L, int Hkv,
   if (rc) return rc;
   if (L < 1 || Hkv < 1 || (int64_t)L * Hkv > kMaxGridY) return HUBKV_EINVAL;
   if ((rc = check_kept(st, kept, n_sink, n_recent, true))) return rc;
-  if (!z || !idx || !aligned(z, 4) || !aligned(idx, 4)) return HUBKV_EALIGN;
+  const int64_t K = kept_total(st);
+  if (!z || !aligned(z, 4) || (K > 0 && (!idx || !aligned(idx, 4)))) return HUBKV_EALIGN;
+  if (K == 0) return HUBKV_OK;  // nothing kept: no row to write
   if (!msel_fits(st, L, Hkv))
     return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, (hipStream_t)stream));
   const MselGeom geo = msel_geometry(st, L, Hkv);
@@ -489,7 +499,8 @@ int hubkv_refine_select(const float* s, int B, const int64_t* seqlens, int L, in
   if (!(isfinite(beta_lo) && isfinite(beta_hi) && beta_lo <= beta_hi)) return HUBKV_EINVAL;
   if (!(r >= 0.f && r <= 1.f)) return HUBKV_EINVAL;
   if ((rc = check_kept(st, kept, n_sink, n_recent, true))) return rc;
-  if (!s || !z || !idx || !aligned(s, 4) || !aligned(z, 4) || !aligned(idx, 4))
+  const int64_t K = kept_total(st);
+  if (!s || !z || !aligned(s, 4) || !aligned(z, 4) || (K > 0 && (!idx || !aligned(idx, 4))))
     return HUBKV_EALIGN;
   if ((head_stats && !aligned(head_stats, 8)) || (beta_in && !aligned(beta_in, 4)) ||
       (beta_out && !aligned(beta_out, 4)))
@@ -500,7 +511,7 @@ int hubkv_refine_select(const float* s, int B, const int64_t* seqlens, int L, in
   if ((uintptr_t)s < (uintptr_t)z + n && (uintptr_t)z < (uintptr_t)s + n) return HUBKV_EINVAL;
   const RefineGeom rg = refine_geometry(rt, L, Hkv);
   const size_t roff = (rg.bytes + 255) & ~(size_t)255;
-  const bool many = msel_fits(st, L, Hkv);
+  const bool many = K > 0 && msel_fits(st, L, Hkv);
   const MselGeom geo = many ? msel_geometry(st, L, Hkv) : MselGeom{};
   if (!workspace || workspace_bytes < roff + (many ? geo.bytes : 256)) return HUBKV_EWORKSPACE;
   if (!aligned(workspace, 256)) return HUBKV_EALIGN;
@@ -517,7 +528,7 @@ int hubkv_refine_select(const float* s, int B, const int64_t* seqlens, int L, in
   if (!many) {
     rc = hip_status(launch_refine(s, rt, L, Hkv, stats, beta_in, pool, gamma, beta_lo, beta_hi,
                                   r2, z, beta_out, strm));
-    if (rc) return rc;
+    if (rc || K == 0) return rc;  // nothing kept: z is the whole result
     return hip_status(launch_select(z, st, L, Hkv, n_sink, n_recent, idx, strm));
   }
   const RefineParams rp{pool, gamma, r2, beta_lo, beta_hi, beta_in, stats, beta_out};
@@ -547,6 +558,7 @@ int hubkv_compact_strided(const void* k_in, const int64_t* k_in_strides, const v
   if ((rc = check_strides(v_in_strides, in_ext, esize, d, false))) return rc;
   if ((rc = check_strides(k_out_strides, out_ext, esize, d, true))) return rc;
   if ((rc = check_strides(v_out_strides, out_ext, esize, d, true))) return rc;
+  if (K == 0) return HUBKV_OK;  // nothing kept: no row to move
   if (!k_in || !v_in || !k_out || !v_out || !idx) return HUBKV_EALIGN;
   if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
       !aligned(idx, 4))
@@ -603,8 +615,11 @@ int hubkv_select_layer(const float* z, int B, const int64_t* seqlens, int L, int
   LselArgs a;
   int rc = make_lsel(a, B, seqlens, L, Hkv, layer_kept, n_sink, n_recent, floor_min);
   if (rc) return rc;
-  if (!z || !idx || !head_kept || !workspace) return HUBKV_EALIGN;
-  if (!aligned(z, 4) || !aligned(idx, 4) || !aligned(head_kept, 4) || !aligned(workspace, 256))
+  int64_t K = 0;
+  for (int i = 0; i < L * B; ++i) K += layer_kept[i];
+  if (!z || !head_kept || !workspace || (K > 0 && !idx)) return HUBKV_EALIGN;
+  if (!aligned(z, 4) || (idx && !aligned(idx, 4)) || !aligned(head_kept, 4) ||
+      !aligned(workspace, 256))
     return HUBKV_EALIGN;
   const LselGeom g = lsel_geometry(a);
   if (workspace_bytes < g.bytes) return HUBKV_EWORKSPACE;
@@ -620,6 +635,9 @@ int hubkv_compact_layer(const void* k_in, const void* v_in, int dtype, const int
   LselArgs a;
   // the budgets only set the row offsets here: no floor or window bound applies
   if ((rc = make_lsel(a, B, seqlens, L, Hkv, layer_kept, 0, 0, 0))) return rc;
+  int64_t K = 0;
+  for (int i = 0; i < L * B; ++i) K += layer_kept[i];
+  if (K == 0) return HUBKV_OK;  // nothing kept: no row to move
   if (!k_in || !v_in || !k_out || !v_out || !idx || !head_kept) return HUBKV_EALIGN;
   if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
       !aligned(idx, 4) || !aligned(head_kept, 4))
