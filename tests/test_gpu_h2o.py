@@ -186,6 +186,18 @@ def test_free_running_stream(dtype, include_self):
     assert frac <= 0.5
 
 
+@pytest.mark.parametrize("heavy,recent,n_sink", [(1, 0, 0), (0, 1, 0), (1, 0, 1), (1, 1, 0),
+                                                  (1, 1, 1), (2, 0, 0), (0, 2, 0), (1, 2, 1),
+                                                  (2, 0, 2), (3, 2, 0)])
+@pytest.mark.parametrize("include_self", [0, 1])
+def test_degenerate_caches(heavy, recent, n_sink, include_self):
+    # caches of 1 to 5 slots from an empty state, windows of size 0 up to the
+    # whole cache (every retained token protected: the token leaving the
+    # recent window, or the new token itself, is then the only candidate)
+    w = S.workload(4).with_(B=2, Hq=4, Hkv=2, d=64, heavy=heavy, recent=recent, dtype="f32")
+    _stream_case(w, 40, n_sink, recent, include_self, 1e-4)
+
+
 def test_literal_budget3_algorithm1_on_gpu():
     gold = json.load(open(os.path.join(GOLD, "h2o_alg1_budget3_literal.json")))
     w = S.H2O_TINY
